@@ -1,0 +1,286 @@
+"""Benchmark of RocketKV's hot path on one MI355X.
+
+Workload (default): the Llama3.1-8B-shaped layer at 128K context, bf16 (32 query / 8 KV heads,
+head dim 128, batch 1; SnapKV++ window 32, pooling kernel 63, keep 16384; decode page size 4,
+top 32 of 128 channels, top-k in {128, 512, 2048}, 256 decode steps each). To keep the
+compressed state from being served by the 256 MB Infinity Cache, the layer is replicated as R
+independently drawn layers (default 8, 640 MiB of compressed K/V + summaries) and consecutive
+decode steps rotate through them, as a multi-layer model would.
+
+One bench step = the whole hot path over that input: SnapKV++ eviction of every replica, page
+summaries of every replica, then all decode steps (channel selection + approximate page scores,
+page top-k, sparse attention) for each top-k. Inputs are drawn on the GPU before timing.
+
+value = mean decode-step latency (us) over the timed steps; the JSON line also carries per-top-k
+latency and GB/s, the per-stage split, the dominant kernel's roofline, and the CPU oracle's time
+on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(w, topk: int) -> dict:
+    """Bytes the method must move per decode step and per stage launch (one layer)."""
+    e = w.elem_bytes
+    B, Hq, Hkv, D, P, r = w.B, w.Hq, w.Hkv, w.D, w.P, w.r
+    n_pages = min(topk // w.page_size, P)
+    k_tok = n_pages * w.page_size
+    approx = B * Hkv * r * P * e + B * Hq * D * e + B * Hkv * P * 4
+    topk_b = B * Hkv * P * 4 + B * Hkv * n_pages * 4
+    attend = 2 * B * Hkv * k_tok * D * e + 2 * B * Hq * D * e + B * Hkv * n_pages * 4
+    step = Hkv * e * (r * P + 2 * k_tok * D) * B + 2 * B * Hq * D * e + B * Hkv * n_pages * 4
+    summaries = B * Hkv * w.Lc * D * e + 2 * B * Hkv * P * D * e
+    evict = (B * Hkv * w.L * D * e + B * w.Hq * w.W * D * e + 4 * B * Hkv * w.keep * D * e
+             + B * Hkv * w.keep * 4)
+    return dict(step=step, approx=approx, topk=topk_b, attend=attend, summaries=summaries,
+                evict=evict)
+
+
+def cpu_baseline(w, sample_steps: int):
+    """The oracle, as it stands, on one KV head of the workload; scaled to us per decode step."""
+    import numpy as np
+    from oracle import rocketkv as O
+    from workloads import generate as gen
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    hd = gen.prompt_head(w, 0, 0, 0)
+    q_win = O.widen(gen.to_storage(hd["q_win"], w.dtype))
+    k = O.widen(gen.to_storage(hd["k"], w.dtype))
+    v = O.widen(gen.to_storage(hd["v"], w.dtype))
+    scale = 1.0 / math.sqrt(w.D)
+    t0 = time.perf_counter()
+    kept, _, _ = O.snapkvpp_head(q_win, k, w.keep, w.pool_kernel, scale)
+    t_evict = time.perf_counter() - t0
+    kc, vc = k[kept], v[kept]
+    kmin, kmax = O.page_summaries(kc, w.page_size)
+    rng = np.random.default_rng(0)
+    per_k = {}
+    for tk in w.topk:
+        n_pages = min(tk // w.page_size, w.P)
+        t0 = time.perf_counter()
+        for _ in range(sample_steps):
+            qg = rng.standard_normal((w.G, w.D))
+            chans, qbar = O.select_channels(qg, w.r)
+            sc = O.approx_page_scores(qbar, chans, kmin, kmax)
+            pages = O.select_pages(sc, n_pages)
+            O.sparse_attention(qg, kc, vc, O.page_tokens(pages, w.page_size, w.Lc), scale)
+        per_k[tk] = (time.perf_counter() - t0) / sample_steps * 1e6 * w.Hkv * w.B
+    value = sum(per_k.values()) / len(per_k)
+    return dict(value=round(value, 1), unit="us per decode step", cores=blas_threads,
+                host_cores_available=cores, kind="oracle",
+                sample=(f"1 of {w.B * w.Hkv} KV heads: SnapKV++ eviction once "
+                        f"({t_evict:.2f} s) and {sample_steps} decode steps per top-k "
+                        f"{list(w.topk)}, scaled x{w.B * w.Hkv} heads; mean over top-k"),
+                per_topk_us={str(k): round(x, 1) for k, x in per_k.items()},
+                evict_s_per_layer=round(t_evict * w.B * w.Hkv, 2))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b-L131072-bf16")
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--cpu-sample-steps", type=int, default=24)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the RocketKV path here runs on a single MI355X "
+              "(no sharding or collectives are built); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sparse_kv_cache_snapkv_amd as rkv
+    from workloads import configs, generate as gen
+
+    w = configs.by_name(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R = args.replicas
+    nsteps = args.decode_steps or w.steps
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dcode = 1 if w.dtype == "bf16" else 0
+    B, Hq, Hkv, D, Lc, P, G = w.B, w.Hq, w.Hkv, w.D, w.Lc, w.P, w.G
+    scale = 1.0 / math.sqrt(D)
+
+    # ---- inputs resident in HBM, outputs and workspaces preallocated
+    prompts = [gen.device_prompt_layer(w, layer, dev) for layer in range(R)]
+    for p in prompts:
+        del p["needle_dir"]
+    q_dec = gen.device_decode_queries(w, 0, nsteps, dev)
+    kept = torch.empty((R, B, Hkv, Lc), dtype=torch.int32, device=dev)
+    k_c = torch.empty((R, B, Hkv, Lc, D), dtype=dt, device=dev)
+    v_c = torch.empty_like(k_c)
+    kmin = torch.empty((R, B, Hkv, D, P), dtype=dt, device=dev)
+    kmax = torch.empty_like(kmin)
+    ev_ws = torch.empty(max(1, rkv.snapkvpp_workspace_bytes(B, Hq, Hkv, w.L, D, w.W, w.keep, dcode)),
+                        dtype=torch.uint8, device=dev)
+    scores = torch.empty((B, Hkv, P), dtype=torch.float32, device=dev)
+    pages = {tk: torch.empty((B, Hkv, min(tk // w.page_size, P)), dtype=torch.int32, device=dev)
+             for tk in w.topk}
+    att_ws = {tk: torch.empty(max(1, rkv.sparse_attend_workspace_bytes(
+        B, Hq, Hkv, D, w.page_size, pages[tk].shape[-1], dcode)), dtype=torch.uint8, device=dev)
+        for tk in w.topk}
+    out = torch.empty((B, Hq, D), dtype=dt, device=dev)
+
+    def evict(r):
+        p = prompts[r]
+        rkv.rkv_snapkvpp_evict(p["q_win"], p["k"], p["v"], w.keep, w.pool_kernel, "avg", scale,
+                               kept_idx=kept[r], k_out=k_c[r], v_out=v_c[r], workspace=ev_ws)
+
+    def summarize(r):
+        rkv.rkv_build_page_summaries(k_c[r], w.page_size, kmin_t=kmin[r], kmax_t=kmax[r])
+
+    def approx(s, r):
+        rkv.rkv_hybrid_approx_scores(q_dec[s], kmin[r], kmax[r], w.r, page_scores=scores)
+
+    def select(tk):
+        rkv.rkv_topk_select(scores, pages[tk].shape[-1], idx_out=pages[tk])
+
+    def attend(s, r, tk):
+        rkv.rkv_sparse_attend_decode(q_dec[s], k_c[r], v_c[r], pages[tk], w.page_size, scale,
+                                     out=out, workspace=att_ws[tk])
+
+    def one_pass(ev=None):
+        """The whole hot path once. ev: optional dict of stage -> list of (start, end) events."""
+        def rec(stage, fn):
+            if ev is None:
+                fn()
+                return
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev.setdefault(stage, []).append((a, b))
+        for r in range(R):
+            rec("evict", lambda: evict(r))
+        for r in range(R):
+            rec("summaries", lambda: summarize(r))
+        for tk in w.topk:
+            for s in range(nsteps):
+                r = s % R
+                if ev is None:
+                    approx(s, r)
+                    select(tk)
+                    attend(s, r, tk)
+                else:
+                    a = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    rec(f"approx@{tk}", lambda: approx(s, r))
+                    rec(f"topk@{tk}", lambda: select(tk))
+                    rec(f"attend@{tk}", lambda: attend(s, r, tk))
+                    b = torch.cuda.Event(enable_timing=True)
+                    b.record()
+                    ev.setdefault(f"step@{tk}", []).append((a, b))
+
+    # decode-only timing per top-k (clean, no inner events)
+    def decode_loop(tk):
+        for s in range(nsteps):
+            r = s % R
+            approx(s, r)
+            select(tk)
+            attend(s, r, tk)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole passes
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_pass()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3
+    pass_ms = t_start.elapsed_time(t_end) / args.steps
+
+    # decode-only latency per top-k (events around each top-k's full step loop)
+    per_topk = {}
+    for tk in w.topk:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            decode_loop(tk)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (args.steps * nsteps)
+        ab = algorithmic_bytes(w, tk)
+        per_topk[str(tk)] = dict(us_per_step=round(us, 3),
+                                 algorithmic_bytes=ab["step"],
+                                 GBps=round(ab["step"] / (us * 1e-6) / 1e9, 1),
+                                 hbm_frac=round(ab["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4))
+
+    # ---- instrumented passes: HIP events around every stage call (per-stage split, roofline)
+    ev = {}
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        one_pass(ev)
+    torch.cuda.synchronize()
+    stage_us = {k: sum(a.elapsed_time(b) for a, b in v) * 1e3 / len(v) for k, v in ev.items()}
+
+    stages = {}
+    for k, us in stage_us.items():
+        name, _, tk = k.partition("@")
+        ab = algorithmic_bytes(w, int(tk) if tk else w.topk[0])
+        nb = ab.get(name, ab["step"] if name == "step" else None)
+        stages[k] = dict(us=round(us, 3))
+        if nb is not None:
+            stages[k]["algorithmic_bytes"] = nb
+            stages[k]["GBps"] = round(nb / (us * 1e-6) / 1e9, 1)
+
+    # dominant kernel of the decode step at the largest top-k: the stage with the most time
+    tk_main = max(w.topk)
+    cand = {n: stage_us[f"{n}@{tk_main}"] for n in ("approx", "topk", "attend")}
+    dom = max(cand, key=cand.get)
+    ab = algorithmic_bytes(w, tk_main)
+    achieved = ab[dom] / (cand[dom] * 1e-6) / 1e9
+    roofline = dict(kernel={"approx": "k_approx_scores", "topk": "k_topk",
+                            "attend": "k_sparse_attend(+merge)"}[dom] + f" @top-k {tk_main}",
+                    bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                    algorithmic_bytes_per_launch=ab[dom], avg_launch_us=round(cand[dom], 3))
+
+    value = sum(v["us_per_step"] for v in per_topk.values()) / len(per_topk)
+    line = dict(
+        metric="decode-step sparse attention latency (us) + achieved HBM GB/s, 8B shape @128K",
+        value=round(value, 3), unit="us", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(pass_ms, 3), higher_is_better=False, scaling="weak", vs_baseline=None,
+        dtype=w.dtype, data="synthetic",
+        config=dict(workload=w.name, batch=B, query_heads=Hq, kv_heads=Hkv, head_dim=D,
+                    context=w.L, window=w.W, pool_kernel=w.pool_kernel, keep=w.keep,
+                    page_size=w.page_size, channels=w.r, topk=list(w.topk),
+                    decode_steps=nsteps, replicas=R),
+        per_topk=per_topk, stages=stages, roofline=roofline,
+        wall_ms_timed=round(wall_ms, 1))
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_steps)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

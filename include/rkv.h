@@ -1,0 +1,202 @@
+/*
+ * rkv.h - C ABI of an MI355X (gfx950) implementation of RocketKV's hot path:
+ * SnapKV++ permanent KV eviction at prefill and hybrid sparse attention at each decode step.
+ *
+ * Method: "RocketKV: Accelerating Long-Context LLM Inference via Two-Stage KV Cache
+ * Compression" (arXiv 2502.14051). Passages cited below by page and section:
+ *   [summary]   summarizepaper.com summary, "Key points"
+ *   [rebuttal]  paperhub.cn, the authors' rebuttal, by section heading
+ *   [abstract]  pith.science record, abstract (v3)
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers to dense row-major arrays unless stated otherwise. The caller
+ *     owns every buffer, workspaces included; the library never allocates, frees or synchronises
+ *     and keeps no state between calls, so concurrent calls on different streams are safe as
+ *     long as their output and workspace buffers do not overlap.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously.
+ *   - dtype: RKV_F32 (float) or RKV_BF16 (bfloat16 stored as uint16 bit patterns). q, K, V,
+ *     summaries and attention outputs share the call's dtype; scores, pooled scores and all
+ *     accumulation are float32; indices are int32.
+ *   - GQA: query head g uses KV head g / (Hq / Hkv); Hq must be a multiple of Hkv.
+ *   - Return value: RKV_OK (0) or a negative RKV_ERR_* code. All argument checks run on the
+ *     host before anything is enqueued, so a failed call has no side effects. RKV_ERR_LAUNCH
+ *     reports an enqueue failure; faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Every index selection breaks score ties toward the lower index and returns indices in
+ *     ascending order.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RKV_VERSION 1
+
+enum rkv_status {
+  RKV_OK = 0,
+  RKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  RKV_ERR_SHAPE = -2,       /* a size or parameter is out of range or inconsistent */
+  RKV_ERR_DTYPE = -3,       /* unknown dtype */
+  RKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the matching *_workspace_bytes */
+  RKV_ERR_UNSUPPORTED = -5, /* valid but not implemented here (e.g. head dim not 64 or 128) */
+  RKV_ERR_LAUNCH = -6       /* the HIP runtime refused to enqueue a kernel */
+};
+
+enum rkv_dtype { RKV_F32 = 0, RKV_BF16 = 1 };
+enum rkv_pool { RKV_POOL_AVG = 0, RKV_POOL_MAX = 1 };
+
+/* Library version (RKV_VERSION). */
+int rkv_version(void);
+
+/* Static English description of a status code; never NULL. */
+const char* rkv_status_string(int status);
+
+/* ------------------------------------------------------------------------------------------
+ * Stage 1 - SnapKV++ permanent eviction ([rebuttal] "Measurement of Exact-TopK": one-time top-k
+ * filtering of the prompt; "SCBench Results": driven by the queries at the end of the prompt;
+ * "Is Needle Among Evicted Tokens": independent per KV head and layer; [summary] and [rebuttal]
+ * "Novelty of SnapKV++": the GQA enhancement; "Potential Sensitivity to Kernel Size in
+ * SnapKV++": the pooling kernel size).
+ *
+ * For every sequence b and KV head h:
+ *   s[g,i,j] = scale * <q_win[b,g,i,:], k[b,h,j,:]>   for the group's query heads g, window row
+ *              i (prompt position L-W+i) and keys j <= L-W+i (causal);
+ *   A = row softmax of s;  c[j] = sum_{g,i} A[g,i,j] for prefix keys j < L-W;
+ *   pooled = same-size 1D pooling of c with kernel `pool_kernel` (odd) and zero padding
+ *            (RKV_POOL_AVG: box sum / pool_kernel; RKV_POOL_MAX: box maximum);
+ *   kept = the keep-W prefix positions with the highest pooled score, ascending, followed by
+ *          the W window positions L-W .. L-1.  When keep >= L nothing is evicted: kept = 0..L-1.
+ * Lc = min(keep, L) slots per head are produced.
+ *
+ * q_win      [B, Hq, W, D]   queries of the last W prompt positions
+ * k, v       [B, Hkv, L, D]  the prompt's keys and values
+ * kept_idx   [B, Hkv, Lc]    int32 out: kept prompt positions
+ * k_out,v_out[B, Hkv, Lc, D] out: the compressed cache (rows of k, v at kept_idx); both NULL
+ *                            to compute indices only, otherwise both non-NULL
+ * pooled_out [B, Hkv, L-W]   float out, may be NULL: the pooled scores (unused when keep >= L)
+ * scale      softmax scale (1/sqrt(D) for standard attention); must be finite and > 0
+ * Requires 1 <= W <= L, W <= keep, D in {64, 128}, pool_kernel odd >= 1.
+ * ws         device workspace of at least rkv_snapkvpp_workspace_bytes(...) bytes (16-byte
+ *            aligned); contents on entry are ignored.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_snapkvpp_workspace_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep,
+                                 int dtype, size_t* bytes);
+int rkv_snapkvpp_evict(const void* q_win, const void* k, const void* v, int B, int Hq, int Hkv,
+                       int L, int D, int W, int keep, int pool_kernel, int pool_type, float scale,
+                       int dtype, int32_t* kept_idx, void* k_out, void* v_out, float* pooled_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Page summaries ([rebuttal] "Explanation of Calculating Approximate Attention Scores", paper
+ * Figure 3: K is split into pages of consecutive tokens and each page keeps its element-wise
+ * minimum and maximum).
+ *
+ * k_c            [B, Hkv, Lc, D]  compressed keys
+ * kmin_t, kmax_t [B, Hkv, D, P]   out, channel-major, P = ceil(Lc / page_size):
+ *                kmin_t[b,h,c,p] = min over slots t of page p (t < Lc) of k_c[b,h,t,c]; same
+ *                for max. Values are copied exactly (no rounding).
+ * Requires Lc >= 1, page_size >= 1, D in {64, 128}.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_build_page_summaries(const void* k_c, int B, int Hkv, int Lc, int D, int page_size,
+                             int dtype, void* kmin_t, void* kmax_t, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Hybrid approximate page scores ([rebuttal] "Explanation of Calculating Approximate Attention
+ * Scores": the bound max(q*Kmin, q*Kmax) per page, computed only on the head-dim positions
+ * where |q| is large, fetching Kmin or Kmax per position by the sign of q, and GQA-consistent
+ * through the group sums of q and |q|; "Novelty": reduction along both sequence and head dims).
+ *
+ * For every sequence b and KV head h with query heads g of its group:
+ *   a[c] = sum_g |q[b,g,c]|, qbar[c] = sum_g q[b,g,c]    (float32)
+ *   C    = the r channels with the largest a (ties: lower channel), ascending
+ *   page_scores[b,h,p] = sum_{c in C} (qbar[c] >= 0 ? qbar[c]*kmax_t[b,h,c,p]
+ *                                                   : qbar[c]*kmin_t[b,h,c,p])
+ *        which equals sum_{c in C} max(qbar[c]*kmin, qbar[c]*kmax).
+ * q              [B, Hq, D]       decode queries
+ * kmin_t, kmax_t [B, Hkv, D, P]   from rkv_build_page_summaries
+ * chan_idx       [B, Hkv, r]      int32 out, may be NULL: C
+ * page_scores    [B, Hkv, P]      float out
+ * Requires 1 <= r <= D, D in {64, 128}, Hq / Hkv <= 8, P >= 1.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_hybrid_approx_scores(const void* q, const void* kmin_t, const void* kmax_t, int B,
+                             int Hq, int Hkv, int D, int P, int r, int dtype, int32_t* chan_idx,
+                             float* page_scores, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Top-k selection ([rebuttal] "Explanation of Calculating Approximate Attention Scores": select
+ * the pages with higher scores; "Measurement of Exact-TopK": SnapKV's one-time top-k filter).
+ *
+ * scores  [rows, n] float (finite; -0.0 and +0.0 are equal)
+ * idx_out [rows, min(k, n)] int32 out: per row, the indices of the min(k, n) largest scores,
+ *         ties to the lower index, in ascending index order.
+ * Requires rows >= 1, n >= 1, k >= 0 (k == 0 does nothing and idx_out may be NULL). ws may be
+ * NULL when the workspace size is 0.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_topk_workspace_bytes(int rows, int n, int k, size_t* bytes);
+int rkv_topk_select(const float* scores, int rows, int n, int k, int32_t* idx_out, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Sparse exact attention over the selected pages ([rebuttal] "Lack of Direct Latency
+ * Comparison": Step 3, sparse attention on the selected tokens; "Explanation of Calculating
+ * Approximate Attention Scores": all heads of a GQA group share the selection).
+ *
+ * For every sequence b, query head g and its KV head h:
+ *   T = slots t of the listed pages (t = page*page_size + u, u < page_size, t < Lc)
+ *   out[b,g,:] = sum_{t in T} softmax_t(scale * <q[b,g,:], k_c[b,h,t,:]>) * v_c[b,h,t,:]
+ * q         [B, Hq, D]
+ * k_c, v_c  [B, Hkv, Lc, D]
+ * page_idx  [B, Hkv, n_pages] int32 page numbers in [0, ceil(Lc/page_size)), each at most
+ *           once (entries outside that range are ignored)
+ * out       [B, Hq, D] out (dtype of the call; bf16 rounds to nearest even)
+ * Requires 1 <= n_pages <= ceil(Lc/page_size), n_pages <= 262144, D in {64, 128},
+ * Hq / Hkv <= 8, scale finite.
+ * ws        workspace of rkv_sparse_attend_workspace_bytes(...) bytes (may be 0, then NULL ok).
+ * ------------------------------------------------------------------------------------------ */
+int rkv_sparse_attend_workspace_bytes(int B, int Hq, int Hkv, int D, int page_size, int n_pages,
+                                      int dtype, size_t* bytes);
+int rkv_sparse_attend_decode(const void* q, const void* k_c, const void* v_c,
+                             const int32_t* page_idx, int B, int Hq, int Hkv, int Lc, int D,
+                             int page_size, int n_pages, float scale, int dtype, void* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * One hybrid decode step in a single kernel launch: the approximate page scores, the page
+ * top-k (k = n_pages) and the sparse attention of the three calls above ([rebuttal]
+ * "Explanation of Calculating Approximate Attention Scores", "Lack of Direct Latency
+ * Comparison": Steps 1-2 approximate and select, Step 3 attends). Scores and selected pages are
+ * bit-identical to those of the separate calls; the output equals theirs up to float rounding
+ * order.
+ *
+ * q, kmin_t, kmax_t, k_c, v_c, out as in the three calls; n_pages = pages to select (1..P).
+ * chan_idx    [B, Hkv, r]       int32 out, may be NULL
+ * page_scores [B, Hkv, P]       float out, may be NULL (then kept in the workspace)
+ * page_idx    [B, Hkv, n_pages] int32 out, may be NULL: the selected pages, ascending
+ * Requires P = ceil(Lc/page_size) <= 8192 and the limits of the three calls.
+ * ws          rkv_hybrid_decode_workspace_bytes(...) bytes, prepared ONCE after allocation by
+ *             rkv_hybrid_decode_workspace_init (it holds per-head counters that every call
+ *             leaves zero). The blocks of a head synchronise through those counters with a
+ *             bounded wait; the grid never exceeds one block per CU. If a wait ever gave up
+ *             (only possible when other work occupies the GPU's CUs at the same time), the
+ *             uint32 at byte offset 0 of ws becomes nonzero and stays so: that call's output is
+ *             not valid. Calls that overlap in time must not share a workspace.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size,
+                                      int n_pages, int dtype, size_t* bytes);
+int rkv_hybrid_decode_workspace_init(void* ws, size_t ws_bytes, void* stream);
+int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
+                           const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
+                           int D, int page_size, int r, int n_pages, float scale, int dtype,
+                           int32_t* chan_idx, float* page_scores, int32_t* page_idx, void* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

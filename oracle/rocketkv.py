@@ -78,7 +78,7 @@ def window_attention(q_win_grp: np.ndarray, k_head: np.ndarray, scale: float) ->
     """
     G, W, D = q_win_grp.shape
     L = k_head.shape[0]
-    s = scale * np.einsum("gwd,ld->gwl", q_win_grp, k_head)
+    s = scale * (q_win_grp @ k_head.T)
     pos = np.arange(L)[None, :]
     row_pos = (L - W + np.arange(W))[:, None]
     s = np.where((pos <= row_pos)[None], s, -np.inf)

@@ -1,0 +1,253 @@
+"""Python binding of the RocketKV C ABI (include/rkv.h): same call names, torch tensors in and
+out. Argument marshalling only: every step runs in the HIP kernels of librkv.so; torch provides
+device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+F32, BF16 = 0, 1
+POOL = {"avg": 0, "max": 1}
+
+
+class RkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.load().rkv_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise RkvError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype: Optional[torch.dtype] = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _size_query(fn: str, *args: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(fn, getattr(_lib.load(), fn)(*args, ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(t: torch.Tensor, nbytes: int, ws: Optional[torch.Tensor]) -> Tuple[int, int]:
+    if nbytes == 0:
+        return 0, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=t.device)
+    _dev(ws, "workspace")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+# ----------------------------------------------------------------------------- workspace sizes
+
+def snapkvpp_workspace_bytes(B, Hq, Hkv, L, D, W, keep, dtype) -> int:
+    return _size_query("rkv_snapkvpp_workspace_bytes", B, Hq, Hkv, L, D, W, keep, dtype)
+
+
+def topk_workspace_bytes(rows, n, k) -> int:
+    return _size_query("rkv_topk_workspace_bytes", rows, n, k)
+
+
+def sparse_attend_workspace_bytes(B, Hq, Hkv, D, page_size, n_pages, dtype) -> int:
+    return _size_query("rkv_sparse_attend_workspace_bytes", B, Hq, Hkv, D, page_size, n_pages,
+                       dtype)
+
+
+# ----------------------------------------------------------------------------- calls
+
+def rkv_snapkvpp_evict(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: int,
+                       pool_kernel: int, pool_type: str = "avg", scale: Optional[float] = None, *,
+                       kept_idx: Optional[torch.Tensor] = None,
+                       k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                       pooled_out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, indices_only: bool = False):
+    """SnapKV++ eviction. q_win [B,Hq,W,D]; k, v [B,Hkv,L,D] -> (kept_idx, k_c, v_c)."""
+    B, Hq, W, D = q_win.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    dt = _dtype_code(k)
+    Lc = min(keep, L)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if kept_idx is None:
+        kept_idx = torch.empty((B, Hkv, Lc), dtype=torch.int32, device=k.device)
+    if not indices_only:
+        if k_out is None:
+            k_out = torch.empty((B, Hkv, Lc, D), dtype=k.dtype, device=k.device)
+        if v_out is None:
+            v_out = torch.empty((B, Hkv, Lc, D), dtype=k.dtype, device=k.device)
+    nbytes = snapkvpp_workspace_bytes(B, Hq, Hkv, L, D, W, keep, dt)
+    ws, wsb = _workspace(k, nbytes, workspace)
+    _check("rkv_snapkvpp_evict", _lib.load().rkv_snapkvpp_evict(
+        _dev(q_win, "q_win", k.dtype), _dev(k, "k"), _dev(v, "v", k.dtype), B, Hq, Hkv, L, D, W,
+        keep, pool_kernel, POOL[pool_type], scale, dt, _dev(kept_idx, "kept_idx", torch.int32),
+        _dev(k_out, "k_out", k.dtype) if k_out is not None else None,
+        _dev(v_out, "v_out", k.dtype) if v_out is not None else None,
+        _dev(pooled_out, "pooled_out", torch.float32) if pooled_out is not None else None,
+        ws, wsb, _stream(k)))
+    return kept_idx, k_out, v_out
+
+
+def rkv_build_page_summaries(k_c: torch.Tensor, page_size: int, *,
+                             kmin_t: Optional[torch.Tensor] = None,
+                             kmax_t: Optional[torch.Tensor] = None):
+    """k_c [B,Hkv,Lc,D] -> (kmin_t, kmax_t) channel-major [B,Hkv,D,P]."""
+    B, Hkv, Lc, D = k_c.shape
+    P = -(-Lc // page_size)
+    if kmin_t is None:
+        kmin_t = torch.empty((B, Hkv, D, P), dtype=k_c.dtype, device=k_c.device)
+    if kmax_t is None:
+        kmax_t = torch.empty((B, Hkv, D, P), dtype=k_c.dtype, device=k_c.device)
+    _check("rkv_build_page_summaries", _lib.load().rkv_build_page_summaries(
+        _dev(k_c, "k_c"), B, Hkv, Lc, D, page_size, _dtype_code(k_c),
+        _dev(kmin_t, "kmin_t", k_c.dtype), _dev(kmax_t, "kmax_t", k_c.dtype), _stream(k_c)))
+    return kmin_t, kmax_t
+
+
+def rkv_hybrid_approx_scores(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.Tensor, r: int,
+                             *, chan_idx: Optional[torch.Tensor] = None,
+                             page_scores: Optional[torch.Tensor] = None,
+                             return_channels: bool = False):
+    """q [B,Hq,D]; summaries [B,Hkv,D,P] -> page_scores [B,Hkv,P] (and chan_idx [B,Hkv,r])."""
+    B, Hq, D = q.shape
+    Hkv, P = kmin_t.shape[1], kmin_t.shape[3]
+    if page_scores is None:
+        page_scores = torch.empty((B, Hkv, P), dtype=torch.float32, device=q.device)
+    if return_channels and chan_idx is None:
+        chan_idx = torch.empty((B, Hkv, r), dtype=torch.int32, device=q.device)
+    _check("rkv_hybrid_approx_scores", _lib.load().rkv_hybrid_approx_scores(
+        _dev(q, "q"), _dev(kmin_t, "kmin_t", q.dtype), _dev(kmax_t, "kmax_t", q.dtype), B, Hq, Hkv,
+        D, P, r, _dtype_code(q),
+        _dev(chan_idx, "chan_idx", torch.int32) if chan_idx is not None else None,
+        _dev(page_scores, "page_scores", torch.float32), _stream(q)))
+    return (page_scores, chan_idx) if return_channels else page_scores
+
+
+def rkv_topk_select(scores: torch.Tensor, k: int, *, idx_out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores [..., n] float32 -> int32 [..., min(k, n)] ascending indices of the top k."""
+    n = scores.shape[-1]
+    rows = scores.numel() // n
+    kk = min(k, n)
+    if idx_out is None:
+        idx_out = torch.empty((*scores.shape[:-1], kk), dtype=torch.int32, device=scores.device)
+    nbytes = topk_workspace_bytes(rows, n, k)
+    ws, wsb = _workspace(scores, nbytes, workspace)
+    _check("rkv_topk_select", _lib.load().rkv_topk_select(
+        _dev(scores, "scores", torch.float32), rows, n, k, _dev(idx_out, "idx_out", torch.int32),
+        ws, wsb, _stream(scores)))
+    return idx_out
+
+
+def rkv_sparse_attend_decode(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
+                             page_idx: torch.Tensor, page_size: int,
+                             scale: Optional[float] = None, *,
+                             out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q [B,Hq,D]; k_c, v_c [B,Hkv,Lc,D]; page_idx [B,Hkv,n_pages] -> out [B,Hq,D]."""
+    B, Hq, D = q.shape
+    Hkv, Lc = k_c.shape[1], k_c.shape[2]
+    n_pages = page_idx.shape[-1]
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = sparse_attend_workspace_bytes(B, Hq, Hkv, D, page_size, n_pages, dt)
+    ws, wsb = _workspace(q, nbytes, workspace)
+    _check("rkv_sparse_attend_decode", _lib.load().rkv_sparse_attend_decode(
+        _dev(q, "q"), _dev(k_c, "k_c", q.dtype), _dev(v_c, "v_c", q.dtype),
+        _dev(page_idx, "page_idx", torch.int32), B, Hq, Hkv, Lc, D, page_size, n_pages, scale, dt,
+        _dev(out, "out", q.dtype), ws, wsb, _stream(q)))
+    return out
+
+
+def hybrid_decode_workspace_bytes(B, Hq, Hkv, Lc, D, page_size, n_pages, dtype) -> int:
+    return _size_query("rkv_hybrid_decode_workspace_bytes", B, Hq, Hkv, Lc, D, page_size, n_pages,
+                       dtype)
+
+
+def rkv_hybrid_decode_workspace(q: torch.Tensor, Hkv: int, Lc: int, page_size: int,
+                                n_pages: int) -> torch.Tensor:
+    """A prepared workspace for rkv_hybrid_decode_step with q's batch, heads and dtype."""
+    B, Hq, D = q.shape
+    nbytes = hybrid_decode_workspace_bytes(B, Hq, Hkv, Lc, D, page_size, n_pages, _dtype_code(q))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check("rkv_hybrid_decode_workspace_init", _lib.load().rkv_hybrid_decode_workspace_init(
+        ws.data_ptr(), nbytes, _stream(q)))
+    return ws
+
+
+def decode_workspace_status(ws: torch.Tensor) -> int:
+    """The workspace status word (nonzero: a fused step's cross-block wait gave up)."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def rkv_hybrid_decode_step(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.Tensor,
+                           k_c: torch.Tensor, v_c: torch.Tensor, page_size: int, r: int,
+                           n_pages: int, scale: Optional[float] = None, *,
+                           chan_idx: Optional[torch.Tensor] = None,
+                           page_scores: Optional[torch.Tensor] = None,
+                           page_idx: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fused decode step (two launches). q [B,Hq,D]; summaries [B,Hkv,D,P]; k_c, v_c
+    [B,Hkv,Lc,D] -> out [B,Hq,D]. Optional outputs: chan_idx, page_scores, page_idx."""
+    B, Hq, D = q.shape
+    Hkv, Lc = k_c.shape[1], k_c.shape[2]
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = rkv_hybrid_decode_workspace(q, Hkv, Lc, page_size, n_pages)
+    ws, wsb = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    opt = lambda t, n, d: _dev(t, n, d) if t is not None else None  # noqa: E731
+    _check("rkv_hybrid_decode_step", _lib.load().rkv_hybrid_decode_step(
+        _dev(q, "q"), _dev(kmin_t, "kmin_t", q.dtype), _dev(kmax_t, "kmax_t", q.dtype),
+        _dev(k_c, "k_c", q.dtype), _dev(v_c, "v_c", q.dtype), B, Hq, Hkv, Lc, D, page_size, r,
+        n_pages, scale, dt, opt(chan_idx, "chan_idx", torch.int32),
+        opt(page_scores, "page_scores", torch.float32), opt(page_idx, "page_idx", torch.int32),
+        _dev(out, "out", q.dtype), ws, wsb, _stream(q)))
+    return out
+
+
+def hybrid_decode_step(q, k_c, v_c, kmin_t, kmax_t, page_size: int, r: int, topk: int,
+                       scale: Optional[float] = None, *, scores=None, pages=None, out=None,
+                       workspace=None):
+    """One decode step as the three C-ABI calls in order: approx scores, page top-k, attention."""
+    P = kmin_t.shape[-1]
+    if topk % page_size:
+        raise ValueError("topk must be a multiple of page_size")
+    n_pages = min(topk // page_size, P)
+    scores = rkv_hybrid_approx_scores(q, kmin_t, kmax_t, r, page_scores=scores)
+    pages = rkv_topk_select(scores, n_pages, idx_out=pages)
+    out = rkv_sparse_attend_decode(q, k_c, v_c, pages, page_size, scale, out=out,
+                                   workspace=workspace)
+    return out, pages, scores

@@ -1,0 +1,57 @@
+// Hybrid approximate page scores: head-dim reduction to the top-|q| channels of the GQA group
+// and sign-selected Kmin/Kmax page bounds (RocketKV rebuttal, "Explanation of Calculating
+// Approximate Attention Scores"; "Novelty": reduction along sequence and head dims).
+//
+// Block = (page range, b*Hkv+h), one wave: the block ranks the group's channels (a few hundred
+// bytes of q, cache resident) and each lane scores one vector of 16 bytes of consecutive pages,
+// reading only the Kmin or the Kmax row of each chosen channel. The fused decode step uses the
+// same device functions, so both produce identical scores.
+#include "rkv_approx.hpp"
+#include "rkv_common.hpp"
+#include "rkv_launch.hpp"
+
+namespace rkv {
+
+namespace {
+
+constexpr int kThreads = 64;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_approx_scores(
+    const T* __restrict__ q, const T* __restrict__ kmin_t, const T* __restrict__ kmax_t, int Hkv,
+    int G, int D, int P, int r, int vec, int32_t* __restrict__ chan_idx,
+    float* __restrict__ scores) {
+  __shared__ ChannelShared ch;
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
+  select_channels_block<T>(q, b, h, Hkv, G, D, r, ch);
+  if (chan_idx != nullptr && blockIdx.x == 0)
+    for (int j = threadIdx.x; j < r; j += kThreads) chan_idx[(size_t)bh * r + j] = ch.chan[j];
+  const int per_block = kThreads * (vec ? vec16<T>::n : 1);
+  const int p0 = blockIdx.x * per_block;
+  score_page_range<T>(kmin_t + (size_t)bh * D * P, kmax_t + (size_t)bh * D * P, D, P, r, p0,
+                      min(P, p0 + per_block), vec != 0, ch, scores + (size_t)bh * P);
+}
+
+template <typename T>
+hipError_t launch_t(const void* q, const void* kmin_t, const void* kmax_t, int B, int Hq, int Hkv,
+                    int D, int P, int r, int32_t* chan_idx, float* scores, hipStream_t stream) {
+  const int vec = P % vec16<T>::n == 0;
+  const int per_block = kThreads * (vec ? vec16<T>::n : 1);
+  dim3 grid((P + per_block - 1) / per_block, B * Hkv);
+  hipLaunchKernelGGL(k_approx_scores<T>, grid, dim3(kThreads), 0, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(kmin_t),
+                     static_cast<const T*>(kmax_t), Hkv, Hq / Hkv, D, P, r, vec, chan_idx, scores);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_approx_scores(const void* q, const void* kmin_t, const void* kmax_t, int B,
+                                int Hq, int Hkv, int D, int P, int r, int dtype,
+                                int32_t* chan_idx, float* page_scores, hipStream_t stream) {
+  if (dtype == 0)
+    return launch_t<float>(q, kmin_t, kmax_t, B, Hq, Hkv, D, P, r, chan_idx, page_scores, stream);
+  return launch_t<bf16_t>(q, kmin_t, kmax_t, B, Hq, Hkv, D, P, r, chan_idx, page_scores, stream);
+}
+
+}  // namespace rkv

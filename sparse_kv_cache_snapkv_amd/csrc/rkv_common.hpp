@@ -1,0 +1,162 @@
+// Device helpers shared by the RocketKV kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkv {
+
+constexpr int kWave = 64;
+
+// bfloat16 is carried as its 16-bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct elem;
+template <>
+struct elem<float> {
+  static constexpr int bytes = 4;
+};
+template <>
+struct elem<bf16_t> {
+  static constexpr int bytes = 2;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  return bf16_t{f32_to_bf16(x)};
+}
+
+// 16 bytes of elements, unpacked to float. VEC = 4 (float) or 8 (bf16).
+template <typename T>
+struct vec16 {
+  static constexpr int n = 16 / elem<T>::bytes;
+};
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& raw, float (&out)[vec16<T>::n]);
+
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& raw, float (&out)[4]) {
+  out[0] = __uint_as_float(raw.x);
+  out[1] = __uint_as_float(raw.y);
+  out[2] = __uint_as_float(raw.z);
+  out[3] = __uint_as_float(raw.w);
+}
+
+template <>
+__device__ __forceinline__ void unpack16<bf16_t>(const uint4& raw, float (&out)[8]) {
+  out[0] = __uint_as_float(raw.x << 16);
+  out[1] = __uint_as_float(raw.x & 0xffff0000u);
+  out[2] = __uint_as_float(raw.y << 16);
+  out[3] = __uint_as_float(raw.y & 0xffff0000u);
+  out[4] = __uint_as_float(raw.z << 16);
+  out[5] = __uint_as_float(raw.z & 0xffff0000u);
+  out[6] = __uint_as_float(raw.w << 16);
+  out[7] = __uint_as_float(raw.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Non-temporal 16-byte load for data read exactly once (K/V rows of the gathered pages).
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 r;
+  r.x = __builtin_nontemporal_load(&q->x);
+  r.y = __builtin_nontemporal_load(&q->y);
+  r.z = __builtin_nontemporal_load(&q->z);
+  r.w = __builtin_nontemporal_load(&q->w);
+  return r;
+}
+
+// DPP lane permutations inside a row of 16 lanes (VALU ops, no LDS round trip).
+enum : int {
+  kDppXor1 = 0xB1,         // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,         // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,  // lane i <- 7-i within each 8 lanes
+  kDppMirror = 0x140,      // lane i <- 15-i within each row
+  kDppRor8 = 0x128,        // lane i <- (i+8) mod 16 within each row
+};
+
+template <int ctrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// Reductions inside groups of `width` consecutive lanes (a power of two <= 64); every lane of
+// the group ends with the result. Within a row the steps are DPP; wider steps are shuffles.
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (width >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (width >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (width >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (width >= 16) v += dpp<kDppMirror>(v);
+#pragma unroll
+  for (int o = 16; o < width; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <int width>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (width >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+  if constexpr (width >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+  if constexpr (width >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if constexpr (width >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+#pragma unroll
+  for (int o = 16; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Reduction across the lane groups of a wave: lanes l, l+stride, l+2*stride, ... (stride a power
+// of two < 64) all end with the result.
+template <int stride>
+__device__ __forceinline__ float across_sum(float v) {
+  if constexpr (stride == 8) v += dpp<kDppRor8>(v);
+#pragma unroll
+  for (int o = stride < 16 ? 16 : stride; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <int stride>
+__device__ __forceinline__ float across_max(float v) {
+  if constexpr (stride == 8) v = fmaxf(v, dpp<kDppRor8>(v));
+#pragma unroll
+  for (int o = stride < 16 ? 16 : stride; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// float -> uint32 key whose unsigned order is the float order; -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace rkv

@@ -1,0 +1,502 @@
+// SnapKV++ permanent eviction at prefill (RocketKV rebuttal, "Measurement of Exact-TopK":
+// one-time top-k filtering of the prompt; "SCBench Results": scored by the queries at the end of
+// the prompt; summary page and rebuttal "Novelty of SnapKV++": attention summed over the GQA
+// group; "Potential Sensitivity to Kernel Size in SnapKV++": 1D pooling with a chosen kernel).
+//
+// Pipeline per (b, KV head):
+//   pass 1  window logits Q_win K^T (causal for window keys) -> per-chunk row (max, sum of exp)
+//   merge   per-row log-sum-exp (log2 domain)
+//   pass 2  logits again for prefix keys, exp(s - lse) summed over the group's G*W rows -> colsum
+//   pool    zero-padded same-size box average (or max) of colsum
+//   top-k   keep-W prefix positions (shared radix select), then the W window positions
+//   gather  compressed K/V rows
+// bf16 logits use MFMA (v_mfma_f32_32x32x16_bf16): the window rows stay in LDS, every wave
+// streams 64 keys into registers and multiplies them against all row tiles. The dot product's
+// head-dim order is permuted identically in both operands (lane half h takes channels
+// h*D/2 + 8*s .. +8 at k-step s), so each lane reads one contiguous half row of K.
+// fp32 logits use plain FMAs (the small-workload path).
+#include <math.h>
+
+#include "rkv_common.hpp"
+#include "rkv_launch.hpp"
+
+namespace rkv {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kKeysPerSub = 256;  // 4 waves x 64 keys
+
+inline int round32(int x) { return (x + 31) & ~31; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct EvictLayout {
+  int GW, GWp, nchunk1, nsub1, nchunk2, nsub2, nprefix;
+  size_t off_stats, off_lse, off_colsum, off_pooled, total;
+};
+
+EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int dtype) {
+  EvictLayout lo{};
+  const int BH = B * Hkv;
+  lo.GW = (Hq / Hkv) * W;
+  lo.GWp = round32(lo.GW);
+  lo.nprefix = L - W;
+  auto split = [&](int nkeys, int& nchunk, int& nsub) {
+    const int subs = (nkeys + kKeysPerSub - 1) / kKeysPerSub;
+    int want = (512 + BH - 1) / BH;  // about two blocks per CU overall
+    if (want > subs) want = subs;
+    if (want < 1) want = 1;
+    nsub = (subs + want - 1) / want;
+    nchunk = (subs + nsub - 1) / nsub;
+    if (nchunk < 1) nchunk = 1;
+  };
+  split(L, lo.nchunk1, lo.nsub1);
+  if (dtype == 0) {  // the fp32 pass 1 takes one 256-key chunk per block
+    lo.nchunk1 = (L + kThreads - 1) / kThreads;
+    lo.nsub1 = 1;
+  }
+  split(lo.nprefix > 0 ? lo.nprefix : 1, lo.nchunk2, lo.nsub2);
+  size_t off = 0;
+  lo.off_stats = off;
+  off = align256(off + (size_t)BH * lo.nchunk1 * lo.GWp * sizeof(float2));
+  lo.off_lse = off;
+  off = align256(off + (size_t)BH * lo.GWp * sizeof(float));
+  lo.off_colsum = off;
+  off = align256(off + (size_t)BH * (lo.nprefix > 0 ? lo.nprefix : 1) * sizeof(float));
+  lo.off_pooled = off;
+  off = align256(off + (size_t)BH * (lo.nprefix > 0 ? lo.nprefix : 1) * sizeof(float));
+  lo.total = off;
+  return lo;
+}
+
+// ---------------------------------------------------------------------------- MFMA (bf16) passes
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __restrict__ q_win,
+                                                             const bf16_t* __restrict__ k, int L,
+                                                             int W, int GW, int nsub, int nchunk,
+                                                             float scale2,
+                                                             float2* __restrict__ stats) {
+  constexpr int KS = D / 16;
+  constexpr int QS = D + 8;
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  float2* run = reinterpret_cast<float2*>(smem + (size_t)GWp * QS);
+  float2* wst = run + GWp;
+
+  const bf16_t* qg = q_win + (size_t)bh * GW * D;
+  for (int idx = tid; idx < GWp * (D / 8); idx += kThreads) {
+    const int row = idx / (D / 8), c8 = idx % (D / 8);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (row < GW) val = load16(qg + (size_t)row * D + c8 * 8);
+    *reinterpret_cast<uint4*>(smem + (size_t)row * QS + c8 * 8) = val;
+  }
+  for (int r = tid; r < GWp; r += kThreads) run[r] = make_float2(-INFINITY, 0.f);
+  __syncthreads();
+
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int key0 = (chunk * nsub + sub) * kKeysPerSub + wave * 64;
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = min(key0 + kt * 32 + n, L - 1);
+      const bf16_t* kr = k + ((size_t)bh * L + key) * D + hf * (D / 2);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[kt][s] = *reinterpret_cast<const bf16x8*>(kr + s * 8);
+    }
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[kt][i] = 0.f;
+      const uint16_t* qrow = smem + (size_t)(rt * 32 + n) * QS + hf * (D / 2);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrow + s * 8);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][s], qf, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][s], qf, acc[1], 0, 0, 0);
+      }
+      // lane holds window row rt*32+n against keys key0 + kt*32 + 8*(i/4) + 4*hf + i%4
+      const int row = rt * 32 + n;
+      const int lim = row < GW ? L - W + (row % W) : -1;  // last visible key
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          const float v = (key < L && key <= lim) ? acc[kt][i] * scale2 : -INFINITY;
+          acc[kt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float sm = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sm += exp2f(acc[kt][i] - mx);
+      }
+      sm += __shfl_xor(sm, 32, 64);
+      if (hf == 0) wst[wave * GWp + row] = make_float2(mx, sm);
+    }
+    __syncthreads();
+    for (int r = tid; r < GWp; r += kThreads) {
+      float m = run[r].x, l = run[r].y;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float2 x = wst[w * GWp + r];
+        const float M = fmaxf(m, x.x);
+        if (M != -INFINITY) {
+          l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
+          m = M;
+        }
+      }
+      run[r] = make_float2(m, l);
+    }
+    __syncthreads();
+  }
+  for (int r = tid; r < GW; r += kThreads)
+    stats[((size_t)bh * nchunk + chunk) * GWp + r] = run[r];
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __restrict__ q_win,
+                                                              const bf16_t* __restrict__ k,
+                                                              const float* __restrict__ lse,
+                                                              int L, int W, int GW, int nsub,
+                                                              float scale2,
+                                                              float* __restrict__ colsum) {
+  constexpr int KS = D / 16;
+  constexpr int QS = D + 8;
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int nprefix = L - W;
+  float* s_lse = reinterpret_cast<float*>(smem + (size_t)GWp * QS);
+
+  const bf16_t* qg = q_win + (size_t)bh * GW * D;
+  for (int idx = tid; idx < GWp * (D / 8); idx += kThreads) {
+    const int row = idx / (D / 8), c8 = idx % (D / 8);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (row < GW) val = load16(qg + (size_t)row * D + c8 * 8);
+    *reinterpret_cast<uint4*>(smem + (size_t)row * QS + c8 * 8) = val;
+  }
+  for (int r = tid; r < GWp; r += kThreads)
+    s_lse[r] = r < GW ? lse[(size_t)bh * GWp + r] : INFINITY;  // padded rows add exp2(-inf) = 0
+  __syncthreads();
+
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int key0 = (chunk * nsub + sub) * kKeysPerSub + wave * 64;
+    if (key0 >= nprefix) break;  // no barrier below: waves may leave independently
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = min(key0 + kt * 32 + n, nprefix - 1);
+      const bf16_t* kr = k + ((size_t)bh * L + key) * D + hf * (D / 2);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[kt][s] = *reinterpret_cast<const bf16x8*>(kr + s * 8);
+    }
+    float cs[2] = {0.f, 0.f};
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[kt][i] = 0.f;
+      const uint16_t* qrow = smem + (size_t)(rt * 32 + n) * QS + hf * (D / 2);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrow + s * 8);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[0][s], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[1][s], acc[1], 0, 0, 0);
+      }
+      // lane holds key key0 + kt*32 + n against rows rt*32 + 8*(i/4) + 4*hf + i%4
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float ls = s_lse[rt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)];
+        cs[0] += exp2f(acc[0][i] * scale2 - ls);
+        cs[1] += exp2f(acc[1][i] * scale2 - ls);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const float tot = cs[kt] + __shfl_xor(cs[kt], 32, 64);
+      const int key = key0 + kt * 32 + n;
+      if (hf == 0 && key < nprefix) colsum[(size_t)bh * nprefix + key] = tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- fp32 passes
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_win_stats_f32(const float* __restrict__ q_win,
+                                                            const float* __restrict__ k, int L,
+                                                            int W, int GW, int nchunk,
+                                                            float scale2,
+                                                            float2* __restrict__ stats) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  float2* wst = reinterpret_cast<float2*>(smem);  // [4][GW]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int GWp = (GW + 31) & ~31;
+  const int key = chunk * kThreads + tid;
+  const float* kr = k + ((size_t)bh * L + min(key, L - 1)) * D;
+  float kv[D];
+#pragma unroll
+  for (int c = 0; c < D; c += 4) {
+    float x[4];
+    unpack16<float>(load16(kr + c), x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kv[c + e] = x[e];
+  }
+  const float* qg = q_win + (size_t)bh * GW * D;
+  for (int row = 0; row < GW; ++row) {
+    const float* qr = qg + (size_t)row * D;
+    float d = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) d = fmaf(qr[c], kv[c], d);
+    const bool valid = key < L && key <= L - W + (row % W);
+    const float v = valid ? d * scale2 : -INFINITY;
+    const float m = group_max<64>(v);
+    float sm = m != -INFINITY ? exp2f(v - m) : 0.f;
+    sm = group_sum<64>(sm);
+    if (lane == 0) wst[wave * GW + row] = make_float2(m, sm);
+  }
+  __syncthreads();
+  for (int r = tid; r < GW; r += kThreads) {
+    float m = -INFINITY, l = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float2 x = wst[w * GW + r];
+      const float M = fmaxf(m, x.x);
+      if (M != -INFINITY) {
+        l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
+        m = M;
+      }
+    }
+    stats[((size_t)bh * nchunk + chunk) * GWp + r] = make_float2(m, l);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_win_colsum_f32(const float* __restrict__ q_win,
+                                                             const float* __restrict__ k,
+                                                             const float* __restrict__ lse, int L,
+                                                             int W, int GW, float scale2,
+                                                             float* __restrict__ colsum) {
+  const int bh = blockIdx.y;
+  const int key = blockIdx.x * kThreads + threadIdx.x;
+  const int nprefix = L - W;
+  if (key >= nprefix) return;
+  const int GWp = (GW + 31) & ~31;
+  const float* kr = k + ((size_t)bh * L + key) * D;
+  float kv[D];
+#pragma unroll
+  for (int c = 0; c < D; c += 4) {
+    float x[4];
+    unpack16<float>(load16(kr + c), x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kv[c + e] = x[e];
+  }
+  const float* qg = q_win + (size_t)bh * GW * D;
+  const float* lb = lse + (size_t)bh * GWp;
+  float cs = 0.f;
+  for (int row = 0; row < GW; ++row) {
+    const float* qr = qg + (size_t)row * D;
+    float d = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) d = fmaf(qr[c], kv[c], d);
+    cs += exp2f(d * scale2 - lb[row]);
+  }
+  colsum[(size_t)bh * nprefix + key] = cs;
+}
+
+// ---------------------------------------------------------------------------- shared stages
+
+__global__ __launch_bounds__(kThreads) void k_win_lse(const float2* __restrict__ stats, int nchunk,
+                                                      int GW, float* __restrict__ lse) {
+  const int bh = blockIdx.x;
+  const int GWp = (GW + 31) & ~31;
+  for (int r = threadIdx.x; r < GW; r += kThreads) {
+    float m = -INFINITY, l = 0.f;
+    for (int c = 0; c < nchunk; ++c) {
+      const float2 x = stats[((size_t)bh * nchunk + c) * GWp + r];
+      const float M = fmaxf(m, x.x);
+      if (M != -INFINITY) {
+        l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
+        m = M;
+      }
+    }
+    lse[(size_t)bh * GWp + r] = m + log2f(l);
+  }
+}
+
+// Zero-padded same-size pooling of each row; the tile and its halo are staged in LDS.
+__global__ __launch_bounds__(kThreads) void k_pool(const float* __restrict__ colsum, int n,
+                                                   int kernel, int kind,
+                                                   float* __restrict__ pooled) {
+  __shared__ float tile[kThreads + 128];
+  const int bh = blockIdx.y;
+  const int h = kernel / 2;
+  const int j0 = blockIdx.x * kThreads;
+  const float* src = colsum + (size_t)bh * n;
+  for (int i = threadIdx.x; i < kThreads + 2 * h; i += kThreads) {
+    const int j = j0 - h + i;
+    tile[i] = (j >= 0 && j < n) ? src[j] : 0.f;
+  }
+  __syncthreads();
+  const int j = j0 + threadIdx.x;
+  if (j >= n) return;
+  float acc = kind == 0 ? 0.f : tile[threadIdx.x];
+  for (int u = 0; u < kernel; ++u) {
+    const float x = tile[threadIdx.x + u];
+    acc = kind == 0 ? acc + x : fmaxf(acc, x);
+  }
+  pooled[(size_t)bh * n + j] = kind == 0 ? acc / (float)kernel : acc;
+}
+
+// Completes kept_idx (window positions, or the identity when nothing is evicted) and gathers
+// the compressed K/V rows, 16 bytes per lane.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_gather(const T* __restrict__ k,
+                                                     const T* __restrict__ v, int L, int W, int Lc,
+                                                     int identity, int32_t* __restrict__ kept,
+                                                     T* __restrict__ k_out, T* __restrict__ v_out) {
+  constexpr int V = vec16<T>::n;
+  constexpr int LPT = D / V;
+  constexpr int TPB = kThreads / LPT;  // tokens per block
+  const int bh = blockIdx.y;
+  const int t = blockIdx.x * TPB + threadIdx.x / LPT;
+  const int li = threadIdx.x % LPT;
+  if (t >= Lc) return;
+  const int nsel = Lc - W;
+  int src;
+  if (identity) {
+    src = t;
+  } else if (t >= nsel) {
+    src = L - W + (t - nsel);
+  } else {
+    src = kept[(size_t)bh * Lc + t];
+  }
+  if (li == 0 && (identity || t >= nsel)) kept[(size_t)bh * Lc + t] = src;
+  if (k_out == nullptr) return;
+  const size_t si = ((size_t)bh * L + src) * D + li * V;
+  const size_t di = ((size_t)bh * Lc + t) * D + li * V;
+  *reinterpret_cast<uint4*>(k_out + di) = load16(k + si);
+  *reinterpret_cast<uint4*>(v_out + di) = load16(v + si);
+}
+
+template <typename T, int D>
+hipError_t gather(const void* k, const void* v, int BH, int L, int W, int Lc, int identity,
+                  int32_t* kept, void* k_out, void* v_out, hipStream_t stream) {
+  constexpr int TPB = kThreads / (D / vec16<T>::n);
+  dim3 grid((Lc + TPB - 1) / TPB, BH);
+  hipLaunchKernelGGL((k_gather<T, D>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const T*>(k), static_cast<const T*>(v), L, W, Lc, identity, kept,
+                     static_cast<T*>(k_out), static_cast<T*>(v_out));
+  return hipGetLastError();
+}
+
+hipError_t gather_any(int dtype, int D, const void* k, const void* v, int BH, int L, int W, int Lc,
+                      int identity, int32_t* kept, void* k_out, void* v_out, hipStream_t stream) {
+  if (dtype == 0)
+    return D == 64 ? gather<float, 64>(k, v, BH, L, W, Lc, identity, kept, k_out, v_out, stream)
+                   : gather<float, 128>(k, v, BH, L, W, Lc, identity, kept, k_out, v_out, stream);
+  return D == 64 ? gather<bf16_t, 64>(k, v, BH, L, W, Lc, identity, kept, k_out, v_out, stream)
+                 : gather<bf16_t, 128>(k, v, BH, L, W, Lc, identity, kept, k_out, v_out, stream);
+}
+
+template <int D>
+hipError_t scores_bf16(const void* q_win, const void* k, int BH, int L, int W,
+                       const EvictLayout& lo, float scale2, char* ws, hipStream_t stream) {
+  constexpr int QS = D + 8;
+  float2* stats = reinterpret_cast<float2*>(ws + lo.off_stats);
+  float* lse = reinterpret_cast<float*>(ws + lo.off_lse);
+  float* colsum = reinterpret_cast<float*>(ws + lo.off_colsum);
+  const size_t lds1 = (size_t)lo.GWp * QS * 2 + (size_t)lo.GWp * sizeof(float2) * 5;
+  const size_t lds2 = (size_t)lo.GWp * QS * 2 + (size_t)lo.GWp * sizeof(float);
+  if (lds1 > 64 * 1024)
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_stats_mfma<D>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+  if (lds2 > 64 * 1024)
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_colsum_mfma<D>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+  hipLaunchKernelGGL(k_win_stats_mfma<D>, dim3(lo.nchunk1, BH), dim3(kThreads), lds1, stream,
+                     static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), L, W,
+                     lo.GW, lo.nsub1, lo.nchunk1, scale2, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_win_lse, dim3(BH), dim3(kThreads), 0, stream, stats, lo.nchunk1, lo.GW, lse);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_win_colsum_mfma<D>, dim3(lo.nchunk2, BH), dim3(kThreads), lds2, stream,
+                     static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), lse, L, W,
+                     lo.GW, lo.nsub2, scale2, colsum);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t scores_f32(const void* q_win, const void* k, int BH, int L, int W,
+                      const EvictLayout& lo, float scale2, char* ws, hipStream_t stream) {
+  float2* stats = reinterpret_cast<float2*>(ws + lo.off_stats);
+  float* lse = reinterpret_cast<float*>(ws + lo.off_lse);
+  float* colsum = reinterpret_cast<float*>(ws + lo.off_colsum);
+  const int nchunk = lo.nchunk1;
+  hipLaunchKernelGGL(k_win_stats_f32<D>, dim3(nchunk, BH), dim3(kThreads),
+                     (size_t)4 * lo.GW * sizeof(float2), stream, static_cast<const float*>(q_win),
+                     static_cast<const float*>(k), L, W, lo.GW, nchunk, scale2, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_win_lse, dim3(BH), dim3(kThreads), 0, stream, stats, nchunk, lo.GW, lse);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_win_colsum_f32<D>, dim3((lo.nprefix + kThreads - 1) / kThreads, BH),
+                     dim3(kThreads), 0, stream, static_cast<const float*>(q_win),
+                     static_cast<const float*>(k), lse, L, W, lo.GW, scale2, colsum);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype) {
+  (void)D;
+  if (keep >= L) return 0;
+  return layout_for(B, Hq, Hkv, L, W, dtype).total;
+}
+
+hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, int Hq, int Hkv,
+                        int L, int D, int W, int keep, int pool_kernel, int pool_type, float scale,
+                        int dtype, int32_t* kept_idx, void* k_out, void* v_out, float* pooled_out,
+                        void* ws, hipStream_t stream) {
+  const int BH = B * Hkv;
+  if (keep >= L)
+    return gather_any(dtype, D, k, v, BH, L, W, L, 1, kept_idx, k_out, v_out, stream);
+  const EvictLayout lo = layout_for(B, Hq, Hkv, L, W, dtype);
+  char* w = static_cast<char*>(ws);
+  const float scale2 = scale * kLog2e;
+  hipError_t e;
+  if (dtype == 0)
+    e = D == 64 ? scores_f32<64>(q_win, k, BH, L, W, lo, scale2, w, stream)
+                : scores_f32<128>(q_win, k, BH, L, W, lo, scale2, w, stream);
+  else
+    e = D == 64 ? scores_bf16<64>(q_win, k, BH, L, W, lo, scale2, w, stream)
+                : scores_bf16<128>(q_win, k, BH, L, W, lo, scale2, w, stream);
+  if (e != hipSuccess) return e;
+  const int n = lo.nprefix;
+  float* colsum = reinterpret_cast<float*>(w + lo.off_colsum);
+  float* pooled = pooled_out != nullptr ? pooled_out : reinterpret_cast<float*>(w + lo.off_pooled);
+  hipLaunchKernelGGL(k_pool, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, stream,
+                     colsum, n, pool_kernel, pool_type, pooled);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_topk(pooled, BH, n, keep - W, kept_idx, keep, nullptr, stream)) != hipSuccess)
+    return e;
+  return gather_any(dtype, D, k, v, BH, L, W, keep, 0, kept_idx, k_out, v_out, stream);
+}
+
+}  // namespace rkv

@@ -1,0 +1,49 @@
+// Internal launchers behind the C ABI. Arguments are validated by the caller (rkv_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rkv {
+
+// Element-wise page min/max of k_c [BH, Lc, D] into channel-major [BH, D, P].
+hipError_t launch_page_minmax(const void* k_c, int BH, int Lc, int D, int page_size, int dtype,
+                              void* kmin_t, void* kmax_t, hipStream_t stream);
+
+// Channel selection and sign-selected page bounds.
+hipError_t launch_approx_scores(const void* q, const void* kmin_t, const void* kmax_t, int B,
+                                int Hq, int Hkv, int D, int P, int r, int dtype,
+                                int32_t* chan_idx, float* page_scores, hipStream_t stream);
+
+// Per-row top-k (ties to the lower index), ascending, rows of out spaced out_stride apart.
+size_t topk_ws_bytes(int rows, int n, int k);
+hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out, int out_stride,
+                       void* ws, hipStream_t stream);
+
+// Exact attention over the selected pages.
+size_t attend_ws_bytes(int B, int Hq, int Hkv, int D, int page_size, int n_pages, int dtype);
+hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
+                                const int32_t* page_idx, int B, int Hq, int Hkv, int Lc, int D,
+                                int page_size, int n_pages, float scale, int dtype, void* out,
+                                void* ws, hipStream_t stream);
+
+// One fused decode step in a single kernel: approximate page scores, page top-k, attention and
+// split merge; the blocks of a head synchronise through counters in the workspace.
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int n_pages,
+                       int dtype);
+hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream);
+hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
+                              const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
+                              int D, int page_size, int r, int n_pages, float scale, int dtype,
+                              int32_t* chan_idx, float* page_scores, int32_t* page_idx, void* out,
+                              void* ws, hipStream_t stream);
+
+// SnapKV++ eviction.
+size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype);
+hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, int Hq, int Hkv,
+                        int L, int D, int W, int keep, int pool_kernel, int pool_type, float scale,
+                        int dtype, int32_t* kept_idx, void* k_out, void* v_out, float* pooled_out,
+                        void* ws, hipStream_t stream);
+
+}  // namespace rkv

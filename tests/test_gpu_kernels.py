@@ -1,0 +1,381 @@
+"""GPU parity of each C-ABI call against the CPU oracle on seeded inputs (small and ragged
+shapes, edge cases). Marked gpu: needs an MI355X and the built librkv.so."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from _parity import TOL_OUT, assert_rows_close, selection_matches
+from oracle import rocketkv as O
+from workloads import configs, generate as gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rkv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_kv_cache_snapkv_amd as rkv
+    rkv._lib.load()
+    return rkv
+
+
+def T(x):
+    return gen.storage_to_torch(x, "cuda")
+
+
+def H(t):
+    return gen.torch_to_storage(t)
+
+
+def _wid(w):
+    return w.name
+
+
+# ----------------------------------------------------------------------------- top-k
+
+TOPK_CASES = [(1, 1), (7, 0), (7, 3), (7, 7), (7, 9), (100, 10), (4096, 32), (4097, 128),
+              (8192, 512), (8193, 1000), (16384, 16), (16385, 4000), (20000, 1234),
+              (131040, 16352)]
+
+
+@pytest.mark.parametrize("n,k", TOPK_CASES)
+def test_topk_select_equals_stable_sort(rkv, n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    s = rng.standard_normal((4, n)).astype(np.float32)
+    s[0, ::3] = 0.5                                  # a large block of exact ties
+    s[1, : n // 2] = 0.0
+    s[1, n // 2::2] = -0.0                           # signed zeros tie
+    s[2] = np.round(s[2], 1)                         # many small tie groups
+    s[3] = np.abs(s[3]) * 1e-3 + 1.0                 # positives sharing the top bits
+    gpu = rkv.rkv_topk_select(torch.from_numpy(s).cuda(), k).cpu().numpy()
+    assert gpu.shape == (4, min(k, n))
+    for r in range(4):
+        assert np.array_equal(gpu[r], O.topk_ascending(s[r].astype(np.float64), k)), r
+
+
+def test_topk_select_all_equal_and_rows_layout(rkv):
+    s = np.full((3, 5000), 2.0, dtype=np.float32)
+    gpu = rkv.rkv_topk_select(torch.from_numpy(s).cuda(), 777).cpu().numpy()
+    assert np.array_equal(gpu, np.tile(np.arange(777), (3, 1)))
+    s3 = np.random.default_rng(5).standard_normal((2, 3, 300)).astype(np.float32)
+    g3 = rkv.rkv_topk_select(torch.from_numpy(s3).cuda(), 20).cpu().numpy()
+    for b in range(2):
+        for h in range(3):
+            assert np.array_equal(g3[b, h], O.topk_ascending(s3[b, h], 20))
+
+
+# ----------------------------------------------------------------------------- summaries
+
+SUMMARY_CASES = [("fp32", 64, 512, 4), ("bf16", 128, 702, 4), ("fp32", 128, 333, 4),
+                 ("bf16", 64, 640, 8), ("bf16", 64, 129, 1), ("bf16", 128, 4100, 4),
+                 ("bf16", 128, 5, 8), ("fp32", 64, 1001, 3)]
+
+
+@pytest.mark.parametrize("dtype,D,Lc,ps", SUMMARY_CASES)
+def test_page_summaries_bit_exact(rkv, dtype, D, Lc, ps):
+    w = configs.SMALL[1].replace(dtype=dtype, D=D, L=Lc, keep=Lc, W=min(8, Lc), n_needles=0,
+                                 B=2, Hq=4, Hkv=2, cfg_id=100 + Lc)
+    k = gen.prompt_layer(w)["k"]
+    kmin, kmax = rkv.rkv_build_page_summaries(T(k), ps)
+    omin, omax = O.summaries(k, ps)
+    assert np.array_equal(O.widen(H(kmin)), omin)
+    assert np.array_equal(O.widen(H(kmax)), omax)
+
+
+# ----------------------------------------------------------------------------- decode calls
+
+def _cache(w, steps=2):
+    """A synthetic compressed cache of Lc slots (drawn like a prompt of length Lc)."""
+    wc = w.replace(L=w.Lc, keep=w.Lc)
+    d = gen.prompt_layer(wc)
+    return wc, d, gen.decode_queries(wc, steps=steps)
+
+
+DECODE_CASES = list(configs.SMALL) + [
+    configs.SMALL[1].replace(name="bf16-P-not-multiple-of-8", keep=1001, cfg_id=20),
+    configs.SMALL[2].replace(name="fp32-P-not-multiple-of-4", keep=501, cfg_id=21, topk=(8, 104)),
+    configs.SMALL[1].replace(name="bf16-g8-d128", Hq=16, Hkv=2, W=16, cfg_id=22),
+]
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=_wid)
+def test_hybrid_approx_scores(rkv, w):
+    wc, d, qs = _cache(w)
+    kmin, kmax = rkv.rkv_build_page_summaries(T(d["k"]), w.page_size)
+    omin, omax = O.summaries(d["k"], w.page_size)
+    G = w.G
+    for s in range(qs.shape[0]):
+        scores, chans = rkv.rkv_hybrid_approx_scores(T(qs[s]), kmin, kmax, w.r,
+                                                     return_channels=True)
+        scores, chans = scores.cpu().numpy(), chans.cpu().numpy()
+        q = O.widen(qs[s])
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                qg = q[b, h * G:(h + 1) * G]
+                selection_matches(chans[b, h], np.abs(qg).sum(0), w.r)
+                # bound over the GPU's channel set (equal to the oracle's up to exact ties)
+                ref = O.approx_page_scores(qg.sum(0), chans[b, h].astype(np.int64), omin[b, h],
+                                           omax[b, h])
+                assert_rows_close(scores[b, h], ref, 1e-5, f"scores b{b} h{h}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_hybrid_approx_scores_wide_grid(rkv, dtype):
+    # enough (b, h) rows x pages that the launch picks the fewest channel groups per block
+    B, Hq, Hkv, D, P, r = 8, 32, 8, 128, 8200, 32
+    rng = np.random.default_rng(41)
+    a = rng.standard_normal((B, Hkv, D, P), dtype=np.float32)
+    b = a + np.abs(rng.standard_normal((B, Hkv, D, P), dtype=np.float32))
+    kmin, kmax = gen.to_storage(a, dtype), gen.to_storage(b, dtype)
+    q = gen.to_storage(rng.standard_normal((B, Hq, D), dtype=np.float32), dtype)
+    scores, chans = rkv.rkv_hybrid_approx_scores(T(q), T(kmin), T(kmax), r, return_channels=True)
+    scores, chans = scores.cpu().numpy(), chans.cpu().numpy()
+    q64, mn, mx = O.widen(q), O.widen(kmin), O.widen(kmax)
+    G = Hq // Hkv
+    for bb in range(B):
+        for h in range(Hkv):
+            qg = q64[bb, h * G:(h + 1) * G]
+            selection_matches(chans[bb, h], np.abs(qg).sum(0), r)
+            ref = O.approx_page_scores(qg.sum(0), chans[bb, h].astype(np.int64), mn[bb, h],
+                                       mx[bb, h])
+            assert_rows_close(scores[bb, h], ref, 1e-5, f"scores b{bb} h{h}")
+
+
+def _random_pages(rng, P, n, force_last=False):
+    if force_last and n < P:
+        sel = np.append(rng.choice(P - 1, size=n - 1, replace=False), P - 1)
+    else:
+        sel = rng.choice(P, size=n, replace=False)
+    return np.sort(sel).astype(np.int32)
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=_wid)
+def test_sparse_attend_decode(rkv, w):
+    wc, d, qs = _cache(w)
+    rng = np.random.default_rng(w.cfg_id)
+    P = w.P
+    kc, vc = O.widen(d["k"]), O.widen(d["v"])
+    scale = 1.0 / math.sqrt(w.D)
+    for n_pages in sorted({1, min(P, 3), min(P, 33), max(1, P // 2), P}):
+        # the first head always lists the (possibly partial) last page
+        pages = np.stack([np.stack([_random_pages(rng, P, n_pages, force_last=(b == 0 and h == 0))
+                                    for h in range(w.Hkv)]) for b in range(w.B)])
+        out = rkv.rkv_sparse_attend_decode(T(qs[0]), T(d["k"]), T(d["v"]),
+                                           torch.from_numpy(pages).cuda(), w.page_size, scale)
+        got = O.widen(H(out))
+        q = O.widen(qs[0])
+        G = w.G
+        ref = np.zeros_like(got)
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                toks = O.page_tokens(pages[b, h], w.page_size, w.Lc)
+                ref[b, h * G:(h + 1) * G] = O.sparse_attention(q[b, h * G:(h + 1) * G], kc[b, h],
+                                                               vc[b, h], toks, scale)
+        assert_rows_close(got, ref, TOL_OUT[w.dtype], f"attend n_pages={n_pages}")
+
+
+def test_sparse_attend_many_splits_bf16(rkv):
+    # a long page list per head exercises the split + log-sum-exp merge path
+    w = configs.SMALL[1].replace(name="long", B=1, Hq=8, Hkv=2, L=12500, keep=12000, cfg_id=30)
+    wc, d, qs = _cache(w, steps=1)
+    rng = np.random.default_rng(3)
+    pages = np.stack([_random_pages(rng, w.P, 2500) for _ in range(w.Hkv)])[None]
+    out = rkv.rkv_sparse_attend_decode(T(qs[0]), T(d["k"]), T(d["v"]),
+                                       torch.from_numpy(pages).cuda(), w.page_size)
+    got = O.widen(H(out))
+    q, kc, vc = O.widen(qs[0]), O.widen(d["k"]), O.widen(d["v"])
+    for h in range(w.Hkv):
+        toks = O.page_tokens(pages[0, h], w.page_size, w.Lc)
+        ref = O.sparse_attention(q[0, h * 4:(h + 1) * 4], kc[0, h], vc[0, h], toks,
+                                 1 / math.sqrt(w.D))
+        assert_rows_close(got[0, h * 4:(h + 1) * 4], ref, TOL_OUT["bf16"])
+
+
+def test_full_budget_is_dense_attention(rkv):
+    w = configs.SMALL[2]
+    wc, d, qs = _cache(w, steps=1)
+    pages = np.tile(np.arange(w.P, dtype=np.int32), (w.B, w.Hkv, 1))
+    out = rkv.rkv_sparse_attend_decode(T(qs[0]), T(d["k"]), T(d["v"]),
+                                       torch.from_numpy(pages).cuda(), w.page_size)
+    q, kc, vc = O.widen(qs[0]), O.widen(d["k"]), O.widen(d["v"])
+    G = w.G
+    kk = torch.from_numpy(np.repeat(kc, G, axis=1))
+    vv = torch.from_numpy(np.repeat(vc, G, axis=1))
+    dense = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None], kk, vv, scale=1 / math.sqrt(w.D))[:, :, 0].numpy()
+    assert_rows_close(O.widen(H(out)), dense, TOL_OUT["fp32"])
+
+
+# ----------------------------------------------------------------------------- eviction
+
+def _evict_check(rkv, w, d, pool="avg", rtol_pooled=1e-4, needles=True):
+    scale = 1.0 / math.sqrt(w.D)
+    pooled = torch.empty((w.B, w.Hkv, max(w.L - w.W, 1)), dtype=torch.float32, device="cuda")
+    kept, kc, vc = rkv.rkv_snapkvpp_evict(T(d["q_win"]), T(d["k"]), T(d["v"]), w.keep,
+                                          w.pool_kernel, pool, scale, pooled_out=pooled)
+    kept = kept.cpu().numpy()
+    ref = O.snapkvpp_evict(d["q_win"], d["k"], d["v"], w.keep, w.pool_kernel, scale, pool)
+    k64, v64 = O.widen(d["k"]), O.widen(d["v"])
+    assert kept.shape == ref["kept"].shape
+    exact = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kp = kept[b, h].astype(np.int64)
+            if w.keep < w.L:
+                assert_rows_close(pooled[b, h].cpu().numpy(), ref["pooled"][b, h], rtol_pooled,
+                                  f"pooled b{b} h{h}")
+                assert list(kp[w.keep - w.W:]) == list(range(w.L - w.W, w.L))
+                exact += selection_matches(kp[:w.keep - w.W], ref["pooled"][b, h], w.keep - w.W)
+                if needles:
+                    assert set(d["needle_pos"][b, h].tolist()) <= set(kp.tolist()), "needle evicted"
+            else:
+                assert np.array_equal(kp, np.arange(w.L))
+            assert np.array_equal(O.widen(H(kc[b, h])), k64[b, h, kp])
+            assert np.array_equal(O.widen(H(vc[b, h])), v64[b, h, kp])
+    return exact
+
+
+@pytest.mark.parametrize("w", configs.SMALL, ids=_wid)
+def test_snapkvpp_evict(rkv, w):
+    d = gen.prompt_layer(w)
+    _evict_check(rkv, w, d)
+
+
+def test_snapkvpp_evict_max_pool_and_limits(rkv):
+    w = configs.SMALL[1]
+    d = gen.prompt_layer(w)
+    _evict_check(rkv, w, d, pool="max")
+    _evict_check(rkv, w.replace(keep=w.W), d, needles=False)  # only the window survives
+    _evict_check(rkv, w.replace(keep=w.L), d)          # nothing evicted
+    _evict_check(rkv, w.replace(keep=w.L + 5), d)      # budget above the prompt
+
+
+def test_evict_indices_only(rkv):
+    w = configs.TINY_FP32
+    d = gen.prompt_layer(w)
+    kept, kc, vc = rkv.rkv_snapkvpp_evict(T(d["q_win"]), T(d["k"]), T(d["v"]), w.keep,
+                                          w.pool_kernel, indices_only=True)
+    assert kc is None and vc is None
+    ref = O.snapkvpp_evict(d["q_win"], d["k"], d["v"], w.keep, w.pool_kernel, 1 / math.sqrt(w.D))
+    for h in range(w.Hkv):
+        selection_matches(kept[0, h, :w.keep - w.W].cpu().numpy(), ref["pooled"][0, h],
+                          w.keep - w.W)
+
+
+def test_error_codes_leave_outputs_untouched(rkv):
+    q = torch.zeros((1, 4, 64), device="cuda")
+    kc = torch.zeros((1, 2, 10, 64), device="cuda")
+    pages = torch.zeros((1, 2, 4), dtype=torch.int32, device="cuda")  # 4 > ceil(10/4)=3 pages
+    out = torch.full((1, 4, 64), 7.0, device="cuda")
+    with pytest.raises(rkv.RkvError) as e:
+        rkv.rkv_sparse_attend_decode(q, kc, kc, pages, 4, out=out)
+    assert e.value.status == -2
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+# ----------------------------------------------------------------------------- fused step
+
+def _fused_vs_calls(rkv, w, q, k_c, v_c, kmin, kmax, topk):
+    """Runs the fused step and the three separate calls; checks identical selections."""
+    n_pages = min(topk // w.page_size, w.P)
+    B, Hq, D = q.shape
+    Hkv = k_c.shape[1]
+    chans = torch.empty((B, Hkv, w.r), dtype=torch.int32, device="cuda")
+    scores = torch.empty((B, Hkv, w.P), dtype=torch.float32, device="cuda")
+    pages = torch.empty((B, Hkv, n_pages), dtype=torch.int32, device="cuda")
+    ws = rkv.rkv_hybrid_decode_workspace(q, Hkv, w.Lc, w.page_size, n_pages)
+    out = rkv.rkv_hybrid_decode_step(q, kmin, kmax, k_c, v_c, w.page_size, w.r, n_pages,
+                                     chan_idx=chans, page_scores=scores, page_idx=pages,
+                                     workspace=ws)
+    s2, c2 = rkv.rkv_hybrid_approx_scores(q, kmin, kmax, w.r, return_channels=True)
+    p2 = rkv.rkv_topk_select(s2, n_pages)
+    o2 = rkv.rkv_sparse_attend_decode(q, k_c, v_c, p2, w.page_size)
+    torch.cuda.synchronize()
+    assert rkv.decode_workspace_status(ws) == 0
+    assert torch.equal(chans, c2)
+    assert torch.equal(scores.view(torch.int32), s2.view(torch.int32)), "scores differ in bits"
+    assert torch.equal(pages, p2)
+    return out, pages, o2
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=_wid)
+def test_fused_decode_step(rkv, w):
+    wc, d, qs = _cache(w)
+    kc_t, vc_t = T(d["k"]), T(d["v"])
+    kmin, kmax = rkv.rkv_build_page_summaries(kc_t, w.page_size)
+    kc, vc = O.widen(d["k"]), O.widen(d["v"])
+    G = w.G
+    for s in range(qs.shape[0]):
+        for topk in sorted(set(w.topk) | {w.page_size, w.P * w.page_size}):
+            out, pages, o2 = _fused_vs_calls(rkv, w, T(qs[s]), kc_t, vc_t, kmin, kmax, topk)
+            got, pg = O.widen(H(out)), pages.cpu().numpy()
+            q = O.widen(qs[s])
+            ref = np.zeros_like(got)
+            for b in range(w.B):
+                for h in range(w.Hkv):
+                    toks = O.page_tokens(pg[b, h], w.page_size, w.Lc)
+                    ref[b, h * G:(h + 1) * G] = O.sparse_attention(
+                        q[b, h * G:(h + 1) * G], kc[b, h], vc[b, h], toks, 1 / math.sqrt(w.D))
+            assert_rows_close(got, ref, TOL_OUT[w.dtype], f"fused step topk={topk}")
+            assert_rows_close(O.widen(H(o2)), ref, TOL_OUT[w.dtype], f"three calls topk={topk}")
+
+
+def test_fused_decode_step_windows_one_block_per_head(rkv):
+    # enough heads that every head gets one block, and more pages than the LDS page buffer
+    w = configs.SMALL[4].replace(name="wide", B=64, Hq=4, Hkv=4, D=64, L=5000, keep=5000,
+                                 page_size=1, r=16, cfg_id=40)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    k_c = torch.randn((w.B, w.Hkv, w.Lc, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    v_c = torch.randn((w.B, w.Hkv, w.Lc, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn((w.B, w.Hq, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    kmin, kmax = rkv.rkv_build_page_summaries(k_c, 1)
+    out, pages, _ = _fused_vs_calls(rkv, w, q, k_c, v_c, kmin, kmax, 2100)
+    got, pg = O.widen(H(out)), pages.cpu().numpy()
+    q64 = O.widen(H(q))
+    for (b, h) in [(0, 0), (17, 2), (63, 3)]:
+        kc = O.widen(H(k_c[b, h]))
+        vc = O.widen(H(v_c[b, h]))
+        ref = O.sparse_attention(q64[b, h:h + 1], kc, vc, pg[b, h].astype(np.int64), 0.125)
+        assert_rows_close(got[b, h:h + 1], ref, TOL_OUT["bf16"], f"b{b} h{h}")
+
+
+def test_fused_decode_step_graph_replays(rkv):
+    w = configs.SMALL[1]
+    wc, d, qs = _cache(w, steps=3)
+    kc_t, vc_t = T(d["k"]), T(d["v"])
+    kmin, kmax = rkv.rkv_build_page_summaries(kc_t, w.page_size)
+    n_pages = w.topk[-1] // w.page_size
+    q_in = T(qs[0]).clone()
+    out = torch.empty_like(q_in)
+    pages = torch.empty((w.B, w.Hkv, n_pages), dtype=torch.int32, device="cuda")
+    ws = rkv.rkv_hybrid_decode_workspace(q_in, w.Hkv, w.Lc, w.page_size, n_pages)
+
+    def step():
+        rkv.rkv_hybrid_decode_step(q_in, kmin, kmax, kc_t, vc_t, w.page_size, w.r, n_pages,
+                                   page_idx=pages, out=out, workspace=ws)
+
+    eager = []
+    for s in range(3):
+        q_in.copy_(T(qs[s]))
+        step()
+        eager.append((out.clone(), pages.clone()))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(6):
+        s = rep % 3
+        q_in.copy_(T(qs[s]))
+        _ = (kc_t.float().sum() + 1.0).item()  # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[s][0]), f"replay {rep} output"
+        assert torch.equal(pages, eager[s][1]), f"replay {rep} pages"
+    assert rkv.decode_workspace_status(ws) == 0
