@@ -9,7 +9,8 @@ decode steps rotate through them, as a multi-layer model would.
 
 One bench step = the whole hot path over that input: SnapKV++ eviction of every replica, page
 summaries of every replica, then all decode steps (channel selection + approximate page scores,
-page top-k, sparse attention) for each top-k. Inputs are drawn on the GPU before timing.
+page top-k, sparse attention: one fused kernel per step) for each top-k. Inputs are drawn on the
+GPU before timing; each stage is captured once as a HIP graph and replayed.
 
 value = mean decode-step latency (us) over the timed steps; the JSON line also carries per-top-k
 latency and GB/s, the per-stage split, the dominant kernel's roofline, and the CPU oracle's time
@@ -134,71 +135,52 @@ def main() -> int:
     kmax = torch.empty_like(kmin)
     ev_ws = torch.empty(max(1, rkv.snapkvpp_workspace_bytes(B, Hq, Hkv, w.L, D, w.W, w.keep, dcode)),
                         dtype=torch.uint8, device=dev)
-    scores = torch.empty((B, Hkv, P), dtype=torch.float32, device=dev)
-    pages = {tk: torch.empty((B, Hkv, min(tk // w.page_size, P)), dtype=torch.int32, device=dev)
-             for tk in w.topk}
-    att_ws = {tk: torch.empty(max(1, rkv.sparse_attend_workspace_bytes(
-        B, Hq, Hkv, D, w.page_size, pages[tk].shape[-1], dcode)), dtype=torch.uint8, device=dev)
-        for tk in w.topk}
-    out = torch.empty((B, Hq, D), dtype=dt, device=dev)
+    n_pages = {tk: min(tk // w.page_size, P) for tk in w.topk}
+    pages = {tk: torch.empty((B, Hkv, n_pages[tk]), dtype=torch.int32, device=dev) for tk in w.topk}
+    dec_ws = {tk: rkv.rkv_hybrid_decode_workspace(q_dec[0], Hkv, Lc, w.page_size, n_pages[tk])
+              for tk in w.topk}
+    out = torch.empty((nsteps, B, Hq, D), dtype=dt, device=dev)
 
-    def evict(r):
-        p = prompts[r]
-        rkv.rkv_snapkvpp_evict(p["q_win"], p["k"], p["v"], w.keep, w.pool_kernel, "avg", scale,
-                               kept_idx=kept[r], k_out=k_c[r], v_out=v_c[r], workspace=ev_ws)
-
-    def summarize(r):
-        rkv.rkv_build_page_summaries(k_c[r], w.page_size, kmin_t=kmin[r], kmax_t=kmax[r])
-
-    def approx(s, r):
-        rkv.rkv_hybrid_approx_scores(q_dec[s], kmin[r], kmax[r], w.r, page_scores=scores)
-
-    def select(tk):
-        rkv.rkv_topk_select(scores, pages[tk].shape[-1], idx_out=pages[tk])
-
-    def attend(s, r, tk):
-        rkv.rkv_sparse_attend_decode(q_dec[s], k_c[r], v_c[r], pages[tk], w.page_size, scale,
-                                     out=out, workspace=att_ws[tk])
-
-    def one_pass(ev=None):
-        """The whole hot path once. ev: optional dict of stage -> list of (start, end) events."""
-        def rec(stage, fn):
-            if ev is None:
-                fn()
-                return
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            ev.setdefault(stage, []).append((a, b))
+    def evict_all():
         for r in range(R):
-            rec("evict", lambda: evict(r))
-        for r in range(R):
-            rec("summaries", lambda: summarize(r))
-        for tk in w.topk:
-            for s in range(nsteps):
-                r = s % R
-                if ev is None:
-                    approx(s, r)
-                    select(tk)
-                    attend(s, r, tk)
-                else:
-                    a = torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    rec(f"approx@{tk}", lambda: approx(s, r))
-                    rec(f"topk@{tk}", lambda: select(tk))
-                    rec(f"attend@{tk}", lambda: attend(s, r, tk))
-                    b = torch.cuda.Event(enable_timing=True)
-                    b.record()
-                    ev.setdefault(f"step@{tk}", []).append((a, b))
+            p = prompts[r]
+            rkv.rkv_snapkvpp_evict(p["q_win"], p["k"], p["v"], w.keep, w.pool_kernel, "avg", scale,
+                                   kept_idx=kept[r], k_out=k_c[r], v_out=v_c[r], workspace=ev_ws)
 
-    # decode-only timing per top-k (clean, no inner events)
-    def decode_loop(tk):
+    def summarize_all():
+        for r in range(R):
+            rkv.rkv_build_page_summaries(k_c[r], w.page_size, kmin_t=kmin[r], kmax_t=kmax[r])
+
+    def decode_all(tk):
+        # one fused kernel per decode step; consecutive steps rotate through the layer replicas
         for s in range(nsteps):
             r = s % R
-            approx(s, r)
-            select(tk)
-            attend(s, r, tk)
+            rkv.rkv_hybrid_decode_step(q_dec[s], kmin[r], kmax[r], k_c[r], v_c[r], w.page_size,
+                                       w.r, n_pages[tk], scale, page_idx=pages[tk], out=out[s],
+                                       workspace=dec_ws[tk])
+
+    # ---- capture each stage as a HIP graph (launch-bound loops replay without host overhead)
+    stages = [("evict", evict_all), ("summaries", summarize_all)] + \
+             [(f"decode@{tk}", (lambda tk=tk: decode_all(tk))) for tk in w.topk]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in stages:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+
+    def one_pass(ev=None):
+        for name, _ in stages:
+            if ev is not None:
+                ev[name][0].record()
+            graphs[name].replay()
+            if ev is not None:
+                ev[name][1].record()
 
     for _ in range(args.warmup):
         one_pass()
@@ -210,59 +192,49 @@ def main() -> int:
     torch.cuda.synchronize()
     t_start.record()
     wall0 = time.perf_counter()
+    stage_ms = {name: 0.0 for name, _ in stages}
     for _ in range(args.steps):
-        one_pass()
+        ev = {name: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for name, _ in stages}
+        one_pass(ev)
+        torch.cuda.synchronize()
+        for name in stage_ms:
+            stage_ms[name] += ev[name][0].elapsed_time(ev[name][1]) / args.steps
     t_end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3
     pass_ms = t_start.elapsed_time(t_end) / args.steps
+    status = {tk: rkv.decode_workspace_status(dec_ws[tk]) for tk in w.topk}
+    if any(status.values()):
+        print(f"warning: a fused decode step reported a synchronisation timeout {status}",
+              file=sys.stderr)
 
-    # decode-only latency per top-k (events around each top-k's full step loop)
     per_topk = {}
-    for tk in w.topk:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(args.steps):
-            decode_loop(tk)
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (args.steps * nsteps)
-        ab = algorithmic_bytes(w, tk)
-        per_topk[str(tk)] = dict(us_per_step=round(us, 3),
-                                 algorithmic_bytes=ab["step"],
-                                 GBps=round(ab["step"] / (us * 1e-6) / 1e9, 1),
-                                 hbm_frac=round(ab["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4))
-
-    # ---- instrumented passes: HIP events around every stage call (per-stage split, roofline)
-    ev = {}
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        one_pass(ev)
-    torch.cuda.synchronize()
-    stage_us = {k: sum(a.elapsed_time(b) for a, b in v) * 1e3 / len(v) for k, v in ev.items()}
-
-    stages = {}
-    for k, us in stage_us.items():
-        name, _, tk = k.partition("@")
+    stages_out = {}
+    for name, ms in stage_ms.items():
+        kind, _, tk = name.partition("@")
         ab = algorithmic_bytes(w, int(tk) if tk else w.topk[0])
-        nb = ab.get(name, ab["step"] if name == "step" else None)
-        stages[k] = dict(us=round(us, 3))
-        if nb is not None:
-            stages[k]["algorithmic_bytes"] = nb
-            stages[k]["GBps"] = round(nb / (us * 1e-6) / 1e9, 1)
+        if kind == "decode":
+            us = ms * 1e3 / nsteps
+            per_topk[tk] = dict(us_per_step=round(us, 3), algorithmic_bytes=ab["step"],
+                                GBps=round(ab["step"] / (us * 1e-6) / 1e9, 1),
+                                hbm_frac=round(ab["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4))
+        else:
+            nb = ab[kind] * R
+            stages_out[name] = dict(us_total=round(ms * 1e3, 2), us_per_layer=round(ms * 1e3 / R, 2),
+                                    algorithmic_bytes=nb, GBps=round(nb / (ms * 1e-3) / 1e9, 1))
 
-    # dominant kernel of the decode step at the largest top-k: the stage with the most time
+    # dominant kernel: the fused decode-step kernel (one launch per step) at the largest top-k;
+    # its launch duration is the graph-replay time per step (kernel plus dispatch gap)
     tk_main = max(w.topk)
-    cand = {n: stage_us[f"{n}@{tk_main}"] for n in ("approx", "topk", "attend")}
-    dom = max(cand, key=cand.get)
+    dom_us = per_topk[str(tk_main)]["us_per_step"]
     ab = algorithmic_bytes(w, tk_main)
-    achieved = ab[dom] / (cand[dom] * 1e-6) / 1e9
-    roofline = dict(kernel={"approx": "k_approx_scores", "topk": "k_topk",
-                            "attend": "k_sparse_attend(+merge)"}[dom] + f" @top-k {tk_main}",
-                    bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+    achieved = ab["step"] / (dom_us * 1e-6) / 1e9
+    roofline = dict(kernel=f"k_decode_step (fused decode step) @top-k {tk_main}", bound="hbm",
+                    achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
-                    algorithmic_bytes_per_launch=ab[dom], avg_launch_us=round(cand[dom], 3))
+                    algorithmic_bytes_per_launch=ab["step"], avg_launch_us=dom_us)
+    stages = stages_out
 
     value = sum(v["us_per_step"] for v in per_topk.values()) / len(per_topk)
     line = dict(
@@ -274,7 +246,7 @@ def main() -> int:
                     context=w.L, window=w.W, pool_kernel=w.pool_kernel, keep=w.keep,
                     page_size=w.page_size, channels=w.r, topk=list(w.topk),
                     decode_steps=nsteps, replicas=R),
-        per_topk=per_topk, stages=stages, roofline=roofline,
+        per_topk=per_topk, stages=stages, roofline=roofline, sync_status=status,
         wall_ms_timed=round(wall_ms, 1))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_steps)

@@ -2,10 +2,11 @@
 // and sign-selected Kmin/Kmax page bounds (RocketKV rebuttal, "Explanation of Calculating
 // Approximate Attention Scores"; "Novelty": reduction along sequence and head dims).
 //
-// Block = (page range, b*Hkv+h), one wave: the block ranks the group's channels (a few hundred
-// bytes of q, cache resident) and each lane scores one vector of 16 bytes of consecutive pages,
-// reading only the Kmin or the Kmax row of each chosen channel. The fused decode step uses the
-// same device functions, so both produce identical scores.
+// Block = (page range, b*Hkv+h): the block ranks the group's channels (a few hundred bytes of q,
+// cache resident); then each quad of lanes scores one 16-byte vector of consecutive pages, each
+// lane summing a quarter of the chosen channels with all of its loads in flight, and only the
+// Kmin or the Kmax row of each channel is read. The fused decode step uses the same device
+// functions, so both produce identical scores.
 #include "rkv_approx.hpp"
 #include "rkv_common.hpp"
 #include "rkv_launch.hpp"
@@ -14,7 +15,7 @@ namespace rkv {
 
 namespace {
 
-constexpr int kThreads = 64;
+constexpr int kThreads = 256;
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_approx_scores(
@@ -26,9 +27,9 @@ __global__ __launch_bounds__(kThreads) void k_approx_scores(
   select_channels_block<T>(q, b, h, Hkv, G, D, r, ch);
   if (chan_idx != nullptr && blockIdx.x == 0)
     for (int j = threadIdx.x; j < r; j += kThreads) chan_idx[(size_t)bh * r + j] = ch.chan[j];
-  const int per_block = kThreads * (vec ? vec16<T>::n : 1);
+  const int per_block = (kThreads / kScoreGroups) * (vec ? vec16<T>::n : 1);
   const int p0 = blockIdx.x * per_block;
-  score_page_range<T>(kmin_t + (size_t)bh * D * P, kmax_t + (size_t)bh * D * P, D, P, r, p0,
+  score_page_range<T, false>(kmin_t + (size_t)bh * D * P, kmax_t + (size_t)bh * D * P, D, P, r, p0,
                       min(P, p0 + per_block), vec != 0, ch, scores + (size_t)bh * P);
 }
 
@@ -36,7 +37,7 @@ template <typename T>
 hipError_t launch_t(const void* q, const void* kmin_t, const void* kmax_t, int B, int Hq, int Hkv,
                     int D, int P, int r, int32_t* chan_idx, float* scores, hipStream_t stream) {
   const int vec = P % vec16<T>::n == 0;
-  const int per_block = kThreads * (vec ? vec16<T>::n : 1);
+  const int per_block = (kThreads / kScoreGroups) * (vec ? vec16<T>::n : 1);
   dim3 grid((P + per_block - 1) / per_block, B * Hkv);
   hipLaunchKernelGGL(k_approx_scores<T>, grid, dim3(kThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(kmin_t),

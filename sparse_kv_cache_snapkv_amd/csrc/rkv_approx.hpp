@@ -77,36 +77,17 @@ __device__ __forceinline__ void select_channels_block(const T* __restrict__ q, i
   __syncthreads();
 }
 
-// Bound of the VMAX consecutive pages starting at p (of one (b, h); P a multiple of VMAX when
-// `vec`, else one page in out[0]). The chosen channels are summed in ascending order, so every
-// kernel that scores pages produces the same bits.
-template <typename T>
-__device__ __forceinline__ void score_page_vector(const T* __restrict__ kmin_bh,
-                                                  const T* __restrict__ kmax_bh, int D, int P,
-                                                  int r, int p, bool vec, const ChannelShared& ch,
-                                                  float (&out)[vec16<T>::n]) {
-  constexpr int VMAX = vec16<T>::n;
-#pragma unroll
-  for (int e = 0; e < VMAX; ++e) out[e] = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < r; ++j) {
-    const float qc = ch.qc[j];
-    const int c = min(max(ch.chan[j], 0), D - 1);
-    const T* row = (qc >= 0.f ? kmax_bh : kmin_bh) + (size_t)c * P + p;
-    if (vec) {
-      float x[VMAX];
-      unpack16<T>(load16(row), x);
-#pragma unroll
-      for (int e = 0; e < VMAX; ++e) out[e] = fmaf(qc, x[e], out[e]);
-    } else {
-      out[0] = fmaf(qc, to_f32(row[0]), out[0]);
-    }
-  }
-}
+// Channel partition of the page-score sum: group g sums chosen channels g, g+4, g+8, ... in
+// ascending order, and the four group sums are combined as (s0 + s1) + (s2 + s3). Every kernel
+// that scores pages uses this order, so they all produce the same bits.
+constexpr int kScoreGroups = 4;
 
-// Scores pages [p_begin, p_end) of one (b, h) into scores_row, one page vector per thread per
-// pass. No barrier.
-template <typename T>
+// Thread layout: lane = 4 * vector + group. Scores the VMAX consecutive pages of vector
+// `pv` = p_begin/V + tid/4 of one (b, h) over [p_begin, p_end) (p_begin a multiple of VMAX when
+// `vec`; `vec` requires P to be a multiple of VMAX, otherwise one page per vector).
+// COHERENT: store with device-coherent (write-through) stores for other blocks to read.
+// No barrier; the whole quad of a vector must be active together.
+template <typename T, bool COHERENT>
 __device__ __forceinline__ void score_page_range(const T* __restrict__ kmin_bh,
                                                  const T* __restrict__ kmax_bh, int D, int P,
                                                  int r, int p_begin, int p_end, bool vec,
@@ -114,15 +95,49 @@ __device__ __forceinline__ void score_page_range(const T* __restrict__ kmin_bh,
                                                  float* __restrict__ scores_row) {
   constexpr int VMAX = vec16<T>::n;
   const int V = vec ? VMAX : 1;
-  for (int p = p_begin + (int)threadIdx.x * V; p < p_end; p += (int)blockDim.x * V) {
-    float s[VMAX];
-    score_page_vector<T>(kmin_bh, kmax_bh, D, P, r, p, vec, ch, s);
-    if (vec && p + VMAX <= p_end) {
-      float4* dst = reinterpret_cast<float4*>(scores_row + p);
+  const int grp = threadIdx.x % kScoreGroups;
+  const int nvec_pass = blockDim.x / kScoreGroups;
+  const int nvec = (p_end - p_begin + V - 1) / V;
+  const int nj = (r - grp + kScoreGroups - 1) / kScoreGroups;  // channels of this group
+  for (int v0 = 0; v0 < nvec; v0 += nvec_pass) {  // uniform trip count across the block
+    const int vi = v0 + (int)threadIdx.x / kScoreGroups;
+    const bool active = vi < nvec;
+    const int p = p_begin + (active ? vi : 0) * V;
+    float acc[VMAX];
 #pragma unroll
-      for (int e = 0; e < VMAX; e += 4) dst[e / 4] = make_float4(s[e], s[e + 1], s[e + 2], s[e + 3]);
-    } else {
-      for (int e = 0; e < V && p + e < p_end; ++e) scores_row[p + e] = s[e];
+    for (int e = 0; e < VMAX; ++e) acc[e] = 0.f;
+    if (active) {
+#pragma unroll 8
+      for (int t = 0; t < nj; ++t) {
+        const int j = grp + t * kScoreGroups;
+        const float qc = ch.qc[j];
+        const int c = min(max(ch.chan[j], 0), D - 1);
+        const T* row = (qc >= 0.f ? kmax_bh : kmin_bh) + (size_t)c * P + p;
+        if (vec) {
+          float x[VMAX];
+          unpack16<T>(load16(row), x);
+#pragma unroll
+          for (int e = 0; e < VMAX; ++e) acc[e] = fmaf(qc, x[e], acc[e]);
+        } else {
+          acc[0] = fmaf(qc, to_f32(row[0]), acc[0]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VMAX; ++e) {
+      acc[e] += dpp<kDppXor1>(acc[e]);
+      acc[e] += dpp<kDppXor2>(acc[e]);
+    }
+    if (active) {
+      // lane `grp` of the quad stores pages grp, grp+4 of its vector (all lanes hold the sums)
+      for (int e = grp; e < V; e += kScoreGroups) {
+        if (p + e < p_end) {
+          if constexpr (COHERENT)
+            __hip_atomic_store(scores_row + p + e, acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            scores_row[p + e] = acc[e];
+        }
+      }
     }
   }
 }

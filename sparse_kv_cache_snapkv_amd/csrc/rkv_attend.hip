@@ -12,7 +12,9 @@
 // by k_attend_merge (log-sum-exp form). The fused decode step (k_decode_step) is one kernel:
 //   1. each block scores its share of its head's pages (rkv_approx.hpp) into the workspace and
 //      arrives on a per-head counter; the blocks of a head wait for each other (bounded spin;
-//      the grid never exceeds one block per CU, so all of them are resident at once);
+//      the grid never exceeds one block per CU, so all of them are resident at once). Data that
+//      crosses blocks (scores, partial results) moves only through device-coherent stores and
+//      loads ordered by s_waitcnt, so no fence has to write back or invalidate the L2;
 //   2. each block runs the exact block top-k (rkv_select.hpp) on all of its head's page scores
 //      and keeps its slice of the ascending page list;
 //   3. attention over that slice;
@@ -313,30 +315,30 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   {
     const int pb_lo = split * a.ppb1, pb_hi = min(a.P, pb_lo + a.ppb1);
     const size_t sbase = (size_t)bh * D * a.P;
-    score_page_range<T>(static_cast<const T*>(a.kmin_t) + sbase,
-                        static_cast<const T*>(a.kmax_t) + sbase, D, a.P, a.r, pb_lo, pb_hi,
-                        a.vec != 0, ch, srow);
+    // written with device-coherent stores: the other blocks of the head read them
+    score_page_range<T, true>(static_cast<const T*>(a.kmin_t) + sbase,
+                              static_cast<const T*>(a.kmax_t) + sbase, D, a.P, a.r, pb_lo, pb_hi,
+                              a.vec != 0, ch, srow);
   }
   if (a.nsplit > 1) {
-    __threadfence();
+    // Exchange through device-coherent accesses only: wait until this block's score stores are
+    // complete, count it in, then poll (relaxed coherent loads) until the whole head is in.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      atomicAdd(arrive, 1u);
+      __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int polls = 0;
-      while (__hip_atomic_load(arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
+      while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
              (unsigned)a.nsplit) {
         if (++polls > kSpinLimit) {
-          atomicOr(a.sync, 1u);  // reported through the workspace status word
+          __hip_atomic_fetch_or(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(2);
       }
     }
-    __syncthreads();
-    __threadfence();
-  } else {
-    __syncthreads();
   }
+  __syncthreads();
 
   // 2 + 3. the head's top pages (this block's slice, in windows of the LDS page buffer), attended
   const int p_lo = split * a.pps;
@@ -359,7 +361,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   } else {
     uint32_t key[E];
     const int i0 = tid * E;
-    const int nv = load_keys<E>(srow, a.P, i0, key);
+    const int nv = a.nsplit > 1 ? load_keys_coherent<E>(srow, a.P, i0, key)
+                                : load_keys<E>(srow, a.P, i0, key);
     uint32_t thr, need_eq;
     block_threshold<kThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, sel);
     int w0 = p_lo;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   st.publish(sh);
   __syncthreads();
 
-  // 4. output, or partial + last-block merge
+  // 4. output, or partial (device-coherent stores) + last-block merge
   T* out = static_cast<T*>(a.out);
   float* hp = a.part + (size_t)bh * a.nsplit * G * (D + 2);
   for (int idx = tid; idx < G * D; idx += kThreads) {
@@ -391,33 +394,37 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
       out[((size_t)bh * G + g) * D + c] = from_f32<T>(lsum > 0.f ? o / lsum : 0.f);
     } else {
       float* pp = hp + ((size_t)split * G + g) * (D + 2);
-      pp[c] = o;
+      __hip_atomic_store(pp + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (c == 0) {
-        pp[D] = M;
-        pp[D + 1] = lsum;
+        __hip_atomic_store(pp + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pp + D + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   if (a.nsplit == 1) return;
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(done, 1u) == (unsigned)(a.nsplit - 1);
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(a.nsplit - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const size_t stride = (size_t)G * (D + 2);
+  auto ld = [](const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, c = idx % D;
     const float* pg = hp + (size_t)g * (D + 2);
     float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(pg + s * stride + D));
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ld(pg + s * stride + D));
     float lsum = 0.f, o = 0.f;
 #pragma unroll 8
     for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = __builtin_nontemporal_load(pg + s * stride + D);
+      const float ms = ld(pg + s * stride + D);
       const float fw = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      lsum = fmaf(__builtin_nontemporal_load(pg + s * stride + D + 1), fw, lsum);
-      o = fmaf(__builtin_nontemporal_load(pg + s * stride + c), fw, o);
+      lsum = fmaf(ld(pg + s * stride + D + 1), fw, lsum);
+      o = fmaf(ld(pg + s * stride + c), fw, o);
     }
     out[((size_t)bh * G + g) * D + c] = from_f32<T>(lsum > 0.f ? o / lsum : 0.f);
   }

@@ -204,4 +204,16 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ row, int n, i
   return n - i0 < 0 ? 0 : (n - i0 > E ? E : n - i0);
 }
 
+// Same, reading through device-coherent loads (scores written by other blocks of the grid).
+template <int E>
+__device__ __forceinline__ int load_keys_coherent(const float* __restrict__ row, int n, int i0,
+                                                  uint32_t (&key)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    key[e] = i0 + e < n ? order_key(__hip_atomic_load(row + i0 + e, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT))
+                        : 0u;
+  return n - i0 < 0 ? 0 : (n - i0 > E ? E : n - i0);
+}
+
 }  // namespace rkv
