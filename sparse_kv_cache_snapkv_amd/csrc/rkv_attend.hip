@@ -49,7 +49,7 @@ struct Geo {
 
 template <int D, int G>
 struct AttendShared {
-  int pages[kMaxPagesPerSplit];
+  int pages[kMaxPagesPerSplit + 1];  // the last slot takes discarded writes
   float m[kWavesPerBlock][G], l[kWavesPerBlock][G];
   float o[kWavesPerBlock][G][D];
 };
@@ -279,33 +279,75 @@ __global__ __launch_bounds__(kThreads) void k_attend_merge(const float* __restri
 
 // ------------------------------------------------------------------------------ fused step
 
+constexpr int kMaxSplit = 64;  // blocks per head in the fused step (one wave polls their flags)
+
 struct StepArgs {
   const void* q;
   const void* kmin_t;
   const void* kmax_t;
   const void* k_c;
   const void* v_c;
-  int Hkv, Lc, ps, n_pages, P, r, pps, ppb1, nsplit, vec;
+  int BH, Hkv, Lc, ps, n_pages, P, r, pps, ppb1, nsplit, nsplit_att, vec;
   float scale2;
   int32_t* chan_idx;  // optional [BH, r]
   float* scores;      // [BH, P]
   int32_t* page_idx;  // optional [BH, n_pages]
-  float* part;        // [BH, nsplit, G, D+2]
-  unsigned* sync;     // [0] status, then (arrive, done) per head
+  float* part;        // [BH, nsplit_att, G, D+2]
+  unsigned* sync;     // [0] status; arrive flags [BH][kMaxSplit]; done flags [BH][kMaxSplit]
   void* out;
 };
+
+__device__ __forceinline__ unsigned ld_coherent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ void st_coherent(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 0 polls flags[lo..hi) (one lane each, one coherent load per poll) until all are set;
+// bounded, on give-up the status word is set. Call from wave 0 only.
+__device__ __forceinline__ void wave_wait_flags(const unsigned* flags, int lo, int hi,
+                                                unsigned* status) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int polls = 0;; ++polls) {
+    const bool mine = lane >= lo && lane < hi;
+    const unsigned f = mine ? ld_coherent(flags + lane) : 1u;
+    if (__all(f != 0u)) return;
+    if (polls > kSpinLimit) {
+      if (lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
 
 template <typename T, int D, int G, int E>
 __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   __shared__ ChannelShared ch;
-  __shared__ AttendShared<D, G> sh;
+  // The head's scores are dead once the keys are in registers (block_threshold passes a barrier
+  // before any page-list or attention write), so they share LDS with the attention scratch.
+  __shared__ union {
+    __align__(16) float scores[E * kThreads];
+    AttendShared<D, G> att;
+  } u;
+  AttendShared<D, G>& sh = u.att;
+  float* s_scores = u.scores;
   __shared__ SelectShared<kThreads> sel;
-  __shared__ int s_last;
-  const int tid = threadIdx.x;
+  __shared__ float s_w[kMaxSplit][G], s_l[kMaxSplit][G];
+  __shared__ float s_inv[G];
+  const int tid = threadIdx.x, wave = tid / kWave;
   const int bh = blockIdx.y, split = blockIdx.x, b = bh / a.Hkv, h = bh % a.Hkv;
   const T* q = static_cast<const T*>(a.q);
-  unsigned* arrive = a.sync + 1 + 2 * bh;
-  unsigned* done = arrive + 1;
+  unsigned* arrive = a.sync + 16 + (size_t)bh * kMaxSplit;
+  unsigned* done = a.sync + 16 + (size_t)a.BH * kMaxSplit + (size_t)bh * kMaxSplit;
+  const bool attends = split < a.nsplit_att;
+
+  WaveState<T, D, G> st;  // the queries' loads overlap the channel selection
+  if (attends) st.init(q + (size_t)bh * G * D, a.scale2);
 
   // 1. this block's share of the head's approximate page scores
   select_channels_block<T>(q, b, h, a.Hkv, G, D, a.r, ch);
@@ -315,36 +357,41 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   {
     const int pb_lo = split * a.ppb1, pb_hi = min(a.P, pb_lo + a.ppb1);
     const size_t sbase = (size_t)bh * D * a.P;
-    // written with device-coherent stores: the other blocks of the head read them
+    // device-coherent stores: the other blocks of the head read them
     score_page_range<T, true>(static_cast<const T*>(a.kmin_t) + sbase,
                               static_cast<const T*>(a.kmax_t) + sbase, D, a.P, a.r, pb_lo, pb_hi,
                               a.vec != 0, ch, srow);
   }
   if (a.nsplit > 1) {
     // Exchange through device-coherent accesses only: wait until this block's score stores are
-    // complete, count it in, then poll (relaxed coherent loads) until the whole head is in.
+    // complete, raise this block's flag, then wait for every block of the head.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-      __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int polls = 0;
-      while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-             (unsigned)a.nsplit) {
-        if (++polls > kSpinLimit) {
-          __hip_atomic_fetch_or(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
+    if (tid == 0) st_coherent(arrive + split, 1u);
+    if (!attends) return;  // a scoring-only block
+    if (wave == 0) wave_wait_flags(arrive, 0, a.nsplit, a.sync);
   }
   __syncthreads();
 
-  // 2 + 3. the head's top pages (this block's slice, in windows of the LDS page buffer), attended
+  // 2. the head's scores into LDS (coalesced), then the top pages of this block's slice
+  if (a.nsplit > 1) {
+    float v[E];  // every load issued before the first use
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = j * kThreads + tid;
+      v[j] = i < a.P ? ld_coherent(srow + i) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = j * kThreads + tid;
+      if (i < a.P) s_scores[i] = v[j];
+    }
+  } else {
+    for (int i = tid; i < a.P; i += kThreads) s_scores[i] = srow[i];
+  }
+  __syncthreads();
   const int p_lo = split * a.pps;
   const int p_hi = min(p_lo + a.pps, a.n_pages);
-  WaveState<T, D, G> st;
-  st.init(q + (size_t)bh * G * D, a.scale2);
   const T* kc_bh = static_cast<const T*>(a.k_c) + (size_t)bh * a.Lc * D;
   const T* vc_bh = static_cast<const T*>(a.v_c) + (size_t)bh * a.Lc * D;
   int32_t* pout = (a.page_idx != nullptr && split == 0) ? a.page_idx + (size_t)bh * a.n_pages
@@ -361,8 +408,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   } else {
     uint32_t key[E];
     const int i0 = tid * E;
-    const int nv = a.nsplit > 1 ? load_keys_coherent<E>(srow, a.P, i0, key)
-                                : load_keys<E>(srow, a.P, i0, key);
+    const int nv = load_keys<E>(s_scores, a.P, i0, key);
     uint32_t thr, need_eq;
     block_threshold<kThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, sel);
     int w0 = p_lo;
@@ -370,67 +416,104 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
       const int nw = min(kMaxPagesPerSplit, max(p_hi - w0, 0));
       const bool write_out = pout != nullptr && w0 == p_lo;
       __syncthreads();
-      block_compact<kThreads, E>(key, nv, thr, need_eq, i0, sel, [&](uint32_t pos, int idx) {
+      block_compact<kThreads, E>(key, nv, thr, need_eq, i0, sel,
+                                 [&](uint32_t pos, int idx, bool take) {
         const int p = (int)pos;
-        if (p >= w0 && p < w0 + nw) sh.pages[p - w0] = idx;
-        if (write_out && p < a.n_pages) pout[p] = idx;
+        // branch-free: elements outside the window go to the spare slot
+        sh.pages[(take && p >= w0 && p < w0 + nw) ? p - w0 : kMaxPagesPerSplit] = idx;
+        if (write_out && take && p < a.n_pages) pout[p] = idx;
       });
       __syncthreads();
       st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc);
       w0 += kMaxPagesPerSplit;
     } while (w0 < p_hi);
   }
+
+  // 3. attention partial of this block
   st.publish(sh);
   __syncthreads();
-
-  // 4. output, or partial (device-coherent stores) + last-block merge
   T* out = static_cast<T*>(a.out);
-  float* hp = a.part + (size_t)bh * a.nsplit * G * (D + 2);
+  const int nsa = a.nsplit_att;
+  float* hp = a.part + (size_t)bh * nsa * G * (D + 2);
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, c = idx % D;
     float M, lsum, o;
     wave_merge<D, G>(sh, g, c, M, lsum, o);
-    if (a.nsplit == 1) {
+    if (nsa == 1) {
       out[((size_t)bh * G + g) * D + c] = from_f32<T>(lsum > 0.f ? o / lsum : 0.f);
     } else {
       float* pp = hp + ((size_t)split * G + g) * (D + 2);
-      __hip_atomic_store(pp + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_coherent(pp + c, o);
       if (c == 0) {
-        __hip_atomic_store(pp + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(pp + D + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_coherent(pp + D, M);
+        st_coherent(pp + D + 1, lsum);
       }
     }
   }
-  if (a.nsplit == 1) return;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(a.nsplit - 1);
-  __syncthreads();
-  if (!s_last) return;
-  const size_t stride = (size_t)G * (D + 2);
-  auto ld = [](const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, c = idx % D;
-    const float* pg = hp + (size_t)g * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ld(pg + s * stride + D));
-    float lsum = 0.f, o = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = ld(pg + s * stride + D);
-      const float fw = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      lsum = fmaf(ld(pg + s * stride + D + 1), fw, lsum);
-      o = fmaf(ld(pg + s * stride + c), fw, o);
+  if (nsa > 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (split != 0) {
+      if (tid == 0) st_coherent(done + split, 1u);
+      return;
     }
-    out[((size_t)bh * G + g) * D + c] = from_f32<T>(lsum > 0.f ? o / lsum : 0.f);
+    // 4. split 0 waits for the other attending blocks, then merges every split
+    if (wave == 0) wave_wait_flags(done, 1, nsa, a.sync);
+    __syncthreads();
+    const size_t stride = (size_t)G * (D + 2);
+    {  // (max, sum) of every split and head into LDS, all loads in flight at once
+      constexpr int kPer = (kMaxSplit * G + kThreads - 1) / kThreads;
+      float mv[kPer], lv[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = j * kThreads + tid;
+        const bool ok = i < nsa * G;
+        const float* pp = hp + (ok ? (i / G) * stride + (i % G) * (D + 2) : 0);
+        mv[j] = ok ? ld_coherent(pp + D) : 0.f;
+        lv[j] = ok ? ld_coherent(pp + D + 1) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = j * kThreads + tid;
+        if (i < nsa * G) {
+          s_w[i / G][i % G] = mv[j];
+          s_l[i / G][i % G] = lv[j];
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float M = -INFINITY;
+      for (int s = 0; s < nsa; ++s) M = fmaxf(M, s_w[s][tid]);
+      float lsum = 0.f;
+      for (int s = 0; s < nsa; ++s) {
+        const float ms = s_w[s][tid];
+        const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+        lsum = fmaf(s_l[s][tid], wgt, lsum);
+        s_w[s][tid] = wgt;
+      }
+      s_inv[tid] = lsum > 0.f ? 1.f / lsum : 0.f;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D, c = idx % D;
+      const float* pc = hp + (size_t)g * (D + 2) + c;
+      float o = 0.f;
+      for (int s0 = 0; s0 < nsa; s0 += 16) {
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = s0 + j < nsa ? ld_coherent(pc + (s0 + j) * stride) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (s0 + j < nsa) o = fmaf(x[j], s_w[s0 + j][g], o);
+      }
+      out[((size_t)bh * G + g) * D + c] = from_f32<T>(o * s_inv[g]);
+    }
   }
-  if (tid == 0) {  // every block of the head has passed both counters: leave them zero
-    __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every block of the head has passed its flags: leave them zero for the next call
+  if (a.nsplit > 1 && tid < a.nsplit) {
+    st_coherent(arrive + tid, 0u);
+    st_coherent(done + tid, 0u);
   }
 }
 
@@ -461,18 +544,22 @@ Plan plan_attend(int BH, int ps, int n_pages) {
   return {ns, pps};
 }
 
-// Fused step: splits only while the whole grid fits one block per CU (the blocks of a head wait
-// for each other); otherwise one block per head.
+// Fused step: scoring blocks per head while the whole grid fits one block per CU (the blocks of
+// a head wait for each other), at most kMaxSplit; the first of them also attend, each to at
+// least one chunk of tokens.
+struct StepPlan {
+  int nsplit, nsplit_att, pps;
+};
+
 template <typename T, int D>
-Plan plan_step(int BH, int ps, int n_pages, int ncu) {
+StepPlan plan_step(int BH, int ps, int n_pages, int ncu) {
   const int ntok = n_pages * ps;
   const int chunk = kWavesPerBlock * Geo<T, D>::WTOK;
-  int ns = max(ncu / BH, 1);
-  ns = min(ns, (ntok + chunk - 1) / chunk);
-  ns = max(min(ns, 256), 1);
-  int pps = (n_pages + ns - 1) / ns;
-  ns = (n_pages + pps - 1) / pps;
-  return {ns, pps};
+  const int ns = max(min(ncu / BH, kMaxSplit), 1);
+  int na = max(min(ns, (ntok + chunk - 1) / chunk), 1);
+  const int pps = (n_pages + na - 1) / na;
+  na = (n_pages + pps - 1) / pps;
+  return {ns, na, pps};
 }
 
 int device_cus() {
@@ -533,7 +620,7 @@ Plan plan_attend_any(int dtype, int D, int BH, int ps, int n_pages) {
   return D == 64 ? plan_attend<bf16_t, 64>(BH, ps, n_pages) : plan_attend<bf16_t, 128>(BH, ps, n_pages);
 }
 
-Plan plan_step_any(int dtype, int D, int BH, int ps, int n_pages, int ncu) {
+StepPlan plan_step_any(int dtype, int D, int BH, int ps, int n_pages, int ncu) {
   if (dtype == 0)
     return D == 64 ? plan_step<float, 64>(BH, ps, n_pages, ncu) : plan_step<float, 128>(BH, ps, n_pages, ncu);
   return D == 64 ? plan_step<bf16_t, 64>(BH, ps, n_pages, ncu) : plan_step<bf16_t, 128>(BH, ps, n_pages, ncu);
@@ -550,7 +637,7 @@ StepLayout step_layout(int B, int Hq, int Hkv, int D, int P, int nsplit_max) {
   const size_t BH = (size_t)B * Hkv;
   StepLayout lo{};
   lo.off_sync = 0;
-  lo.off_scores = align256((1 + 2 * BH) * sizeof(unsigned));
+  lo.off_scores = align256((16 + 2 * BH * kMaxSplit) * sizeof(unsigned));
   lo.off_part = align256(lo.off_scores + BH * P * sizeof(float));
   lo.total = align256(lo.off_part + BH * nsplit_max * (Hq / Hkv) * (D + 2) * sizeof(float));
   return lo;
@@ -581,8 +668,8 @@ hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int n_pages,
                        int dtype) {
   const int P = (Lc + page_size - 1) / page_size;
-  const Plan pl = plan_step_any(dtype, D, B * Hkv, page_size, n_pages, kTargetBlocks);
-  return step_layout(B, Hq, Hkv, D, P, pl.nsplit).total;
+  const StepPlan pl = plan_step_any(dtype, D, B * Hkv, page_size, n_pages, kTargetBlocks);
+  return step_layout(B, Hq, Hkv, D, P, pl.nsplit_att).total;
 }
 
 hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream) {
@@ -600,15 +687,15 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
                               void* ws, hipStream_t stream) {
   const int BH = B * Hkv;
   const int P = (Lc + page_size - 1) / page_size;
-  const Plan pmax = plan_step_any(dtype, D, BH, page_size, n_pages, kTargetBlocks);
-  const Plan pl = plan_step_any(dtype, D, BH, page_size, n_pages, device_cus());
-  const StepLayout lo = step_layout(B, Hq, Hkv, D, P, pmax.nsplit);
+  const StepPlan pmax = plan_step_any(dtype, D, BH, page_size, n_pages, kTargetBlocks);
+  const StepPlan pl = plan_step_any(dtype, D, BH, page_size, n_pages, device_cus());
+  const StepLayout lo = step_layout(B, Hq, Hkv, D, P, pmax.nsplit_att);
   char* w = static_cast<char*>(ws);
   const int vmax = dtype == 0 ? vec16<float>::n : vec16<bf16_t>::n;
   int ppb1 = (P + pl.nsplit - 1) / pl.nsplit;
   ppb1 = (ppb1 + vmax - 1) / vmax * vmax;
-  StepArgs a{q, kmin_t, kmax_t, k_c, v_c, Hkv, Lc, page_size, n_pages, P, r, pl.pps, ppb1,
-             pl.nsplit, P % vmax == 0, scale * kLog2e, chan_idx,
+  StepArgs a{q, kmin_t, kmax_t, k_c, v_c, BH, Hkv, Lc, page_size, n_pages, P, r, pl.pps, ppb1,
+             pl.nsplit, pl.nsplit_att, P % vmax == 0, scale * kLog2e, chan_idx,
              page_scores != nullptr ? page_scores : reinterpret_cast<float*>(w + lo.off_scores),
              page_idx, reinterpret_cast<float*>(w + lo.off_part),
              reinterpret_cast<unsigned*>(w + lo.off_sync), out};

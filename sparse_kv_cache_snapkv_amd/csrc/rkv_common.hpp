@@ -150,11 +150,28 @@ __device__ __forceinline__ float across_max(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: row shifts build per-row (16 lane)
+// sums, then row broadcasts carry row totals into the following rows.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // float -> uint32 key whose unsigned order is the float order; -0.0 maps like +0.0.
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
   if ((u << 1) == 0u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of order_key (the -0.0 -> +0.0 canonicalisation aside).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

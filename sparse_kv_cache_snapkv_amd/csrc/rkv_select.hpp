@@ -5,7 +5,10 @@
 // first reduces the minimum and maximum key: bits above their highest differing bit are common
 // to every element, so the 8-bit radix digits start right below them (the first digit then
 // spreads over bins instead of piling onto one, which matters for LDS histogram atomics).
-// Digit passes narrow the k-th largest key T; an ordered compaction then gives every element
+// Each digit pass counts into per-wave histograms (double-buffered, so a pass needs two
+// barriers) and one wave scans the bins from the top to narrow the k-th largest key T; once
+// the bin holding T has at most kSelectCandidates keys, those keys are gathered and T is found
+// by ranking them against each other directly. An ordered compaction then gives every element
 // above T, and the lowest-index elements equal to T, its position in the ascending list.
 #pragma once
 
@@ -13,12 +16,20 @@
 
 namespace rkv {
 
+constexpr int kSelectCandidates = 256;  // a bin this small is finished by direct ranking
+constexpr int kValueBins = 2048;       // bins of the first, value-linear counting pass
+
 template <int THREADS>
 struct SelectShared {
-  uint32_t hist[256];
-  uint32_t wa[THREADS / kWave];
-  uint32_t wb[THREADS / kWave];
-  uint32_t digit, above;
+  static constexpr int NW = THREADS / kWave;
+  union {
+    uint32_t hist[2][NW][256 + kWave];  // bins 256.. take non-matching keys, one per lane (unread)
+    uint32_t vbins[kValueBins];
+  };
+  uint32_t cand[kSelectCandidates + 1];  // slot kSelectCandidates likewise
+  uint32_t wa[NW];
+  uint32_t wb[NW];
+  uint32_t digit, above, binc, ncand, thr, need;
 };
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -38,16 +49,7 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea
                                             uint32_t& ta, uint32_t& tb, SelectShared<THREADS>& sh) {
   constexpr int NW = THREADS / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  uint32_t ia = a, ib = b;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t xa = __shfl_up(ia, o, kWave);
-    const uint32_t xb = __shfl_up(ib, o, kWave);
-    if (lane >= o) {
-      ia += xa;
-      ib += xb;
-    }
-  }
+  const uint32_t ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
   if (lane == kWave - 1) {
     sh.wa[wave] = ia;
     sh.wb[wave] = ib;
@@ -91,6 +93,8 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
     sh.wa[wave] = lo;
     sh.wb[wave] = hi;
   }
+  // both histogram buffers start at zero
+  for (int i = tid; i < 2 * NW * (256 + kWave); i += THREADS) (&sh.hist[0][0][0])[i] = 0u;
   __syncthreads();
   lo = sh.wa[0];
   hi = sh.wb[0];
@@ -99,32 +103,117 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
     lo = min(lo, sh.wa[w]);
     hi = max(hi, sh.wb[w]);
   }
-  __syncthreads();
   if (lo == hi) {  // all keys equal
     T = lo;
     need_eq = k;
+    __syncthreads();
     return;
   }
-  int bits = 32 - __clz(lo ^ hi);  // low bits that still vary
+  // Pass over value-linear bins between the block's minimum and maximum: the bin index is a
+  // monotone function of the key, so the bin holding the k-th largest key is exact; its keys are
+  // then ranked directly. Clustered values (a large bin) fall back to the radix passes below.
+  {
+    const float flo = key_float(lo), fhi = key_float(hi);
+    const float inv = (float)kValueBins / (fhi - flo);
+    if (isfinite(flo) && isfinite(fhi) && isfinite(inv) && inv > 0.f) {
+      auto bin_of = [&](uint32_t kk) {
+        const int b = (int)((key_float(kk) - flo) * inv);
+        return min(max(b, 0), kValueBins - 1);
+      };
+      for (int i = tid; i < kValueBins; i += THREADS) sh.vbins[i] = 0u;
+      if (tid == 0) sh.ncand = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (e < nvalid) atomicAdd(&sh.vbins[bin_of(key[e])], 1u);
+      __syncthreads();
+      // thread t owns the kValueBins/THREADS bins just below those of thread t-1 (descending)
+      constexpr int BPT = kValueBins / THREADS;
+      uint32_t c[BPT], local = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        c[j] = sh.vbins[kValueBins - 1 - (tid * BPT + j)];
+        local += c[j];
+      }
+      uint32_t excl, unused, tot, unused2;
+      block_scan2<THREADS>(local, 0u, excl, unused, tot, unused2, sh);
+      if (excl < k && k <= excl + local) {
+        uint32_t run = excl;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+          if (run < k && k <= run + c[j]) {
+            sh.digit = (uint32_t)(kValueBins - 1 - (tid * BPT + j));
+            sh.above = run;
+            sh.binc = c[j];
+          }
+          run += c[j];
+        }
+      }
+      __syncthreads();
+      if (sh.binc <= (uint32_t)kSelectCandidates) {
+        const int bstar = (int)sh.digit;
+        const uint32_t krem = k - sh.above;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e < nvalid && bin_of(key[e]) == bstar) {
+            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+            sh.cand[slot < (uint32_t)kSelectCandidates ? slot : (uint32_t)kSelectCandidates] = key[e];
+          }
+        }
+        __syncthreads();
+        const uint32_t nc = sh.ncand;
+        for (uint32_t t = tid; t < nc; t += THREADS) {
+          const uint32_t kt = sh.cand[t];
+          uint32_t gt = 0, ge = 0;
+          for (uint32_t j = 0; j < nc; ++j) {
+            const uint32_t kj = sh.cand[j];
+            gt += kj > kt;
+            ge += kj >= kt;
+          }
+          if (gt < krem && krem <= ge) {
+            sh.thr = kt;
+            sh.need = krem - gt;
+          }
+        }
+        __syncthreads();
+        T = sh.thr;
+        need_eq = sh.need;
+        __syncthreads();
+        return;
+      }
+      // a crowded bin: start the radix passes with clean histograms
+      for (int i = tid; i < 2 * NW * (256 + kWave); i += THREADS) (&sh.hist[0][0][0])[i] = 0u;
+      __syncthreads();
+    }
+  }
+  int bits = 32 - __clz((int)(lo ^ hi));  // low bits that still vary
   uint32_t prefix = bits >= 32 ? 0u : (lo >> bits) << bits;
   uint32_t mask = bits >= 32 ? 0u : ~((1u << bits) - 1u);
   uint32_t krem = k;
+  int buf = 0;
+  bool done = false;
   while (bits > 0) {
     const int shift = bits > 8 ? bits - 8 : 0;
-    if (tid < 256) sh.hist[tid] = 0;
-    __syncthreads();
+    uint32_t* hw = sh.hist[buf][wave];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (e < nvalid && (key[e] & mask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
+    for (int e = 0; e < E; ++e) {  // branch-free: non-matching keys count into the lane's spare bin
+      const bool m = e < nvalid && (key[e] & mask) == prefix;
+      atomicAdd(&hw[m ? ((key[e] >> shift) & 255u) : 256u + lane], 1u);
     }
+    // the other buffer (scanned in the previous pass) is cleared for the next one
+    for (int i = tid; i < NW * (256 + kWave); i += THREADS) (&sh.hist[buf ^ 1][0][0])[i] = 0u;
+    if (tid == 0) sh.ncand = 0;
     __syncthreads();
     if (tid < kWave) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
+      // lane l owns digits 255-4l .. 252-4l (descending), summed over the waves' histograms
       uint32_t c[4], c4 = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = sh.hist[255 - 4 * tid - j];
-        c4 += c[j];
+        uint32_t x = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x += sh.hist[buf][w][255 - 4 * tid - j];
+        c[j] = x;
+        c4 += x;
       }
       uint32_t incl = c4;
 #pragma unroll
@@ -140,6 +229,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
           if (run < krem && krem <= run + c[j]) {
             sh.digit = 255 - 4 * tid - j;
             sh.above = run;
+            sh.binc = c[j];
           }
           run += c[j];
         }
@@ -150,14 +240,47 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
     mask |= 255u << shift;
     krem -= sh.above;
     bits = shift;
-    __syncthreads();
+    buf ^= 1;
+    if (bits > 0 && sh.binc <= (uint32_t)kSelectCandidates) {
+      // gather the bin's keys and rank them directly
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (e < nvalid && (key[e] & mask) == prefix) {
+          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+          sh.cand[slot < (uint32_t)kSelectCandidates ? slot : (uint32_t)kSelectCandidates] = key[e];
+        }
+      }
+      __syncthreads();
+      const uint32_t nc = sh.ncand;
+      for (uint32_t t = tid; t < nc; t += THREADS) {
+        const uint32_t kt = sh.cand[t];
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t j = 0; j < nc; ++j) {
+          const uint32_t kj = sh.cand[j];
+          gt += kj > kt;
+          ge += kj >= kt;
+        }
+        if (gt < krem && krem <= ge) {  // kt is the krem-th largest key of the bin
+          sh.thr = kt;
+          sh.need = krem - gt;
+        }
+      }
+      __syncthreads();
+      prefix = sh.thr;
+      krem = sh.need;
+      done = true;
+      break;
+    }
   }
+  (void)done;
   T = prefix;
   need_eq = krem;
+  __syncthreads();  // sh.digit / sh.above / sh.wa are rewritten by later uses
 }
 
-// Ascending positions of the selected elements. emit(pos, index) is called once per selected
-// element (pos < k). Contains barriers; every thread of the block must call it.
+// Ascending positions of the selected elements. emit(pos, index, selected) is called for every
+// element of the thread (branch-free); pos < k is meaningful only when `selected`. Contains
+// barriers; every thread of the block must call it.
 template <int THREADS, int E, typename Emit>
 __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nvalid, uint32_t T,
                                               uint32_t need_eq, int base_index,
@@ -172,19 +295,18 @@ __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nval
   block_scan2<THREADS>(ngt, neq, bg, be, tg, te, sh);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (e >= nvalid) continue;
-    if (key[e] > T) {
-      emit(bg + (be < need_eq ? be : need_eq), base_index + e);
-      ++bg;
-    } else if (key[e] == T) {
-      if (be < need_eq) emit(bg + be, base_index + e);
-      ++be;
-    }
+    const bool gt = e < nvalid && key[e] > T;
+    const bool eq = e < nvalid && key[e] == T;
+    const bool take = gt || (eq && be < need_eq);
+    const uint32_t pos = bg + (gt ? min(be, need_eq) : be);
+    emit(pos, base_index + e, take);
+    bg += gt;
+    be += eq;
   }
 }
 
 // Loads the E consecutive scores of a row starting at i0 (blocked layout) as keys; returns how
-// many of them exist (0..E).
+// many of them exist (0..E). Works for global and LDS rows.
 template <int E>
 __device__ __forceinline__ int load_keys(const float* __restrict__ row, int n, int i0,
                                          uint32_t (&key)[E]) {
@@ -201,18 +323,6 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ row, int n, i
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = i0 + e < n ? order_key(row[i0 + e]) : 0u;
-  return n - i0 < 0 ? 0 : (n - i0 > E ? E : n - i0);
-}
-
-// Same, reading through device-coherent loads (scores written by other blocks of the grid).
-template <int E>
-__device__ __forceinline__ int load_keys_coherent(const float* __restrict__ row, int n, int i0,
-                                                  uint32_t (&key)[E]) {
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    key[e] = i0 + e < n ? order_key(__hip_atomic_load(row + i0 + e, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT))
-                        : 0u;
   return n - i0 < 0 ? 0 : (n - i0 > E ? E : n - i0);
 }
 
