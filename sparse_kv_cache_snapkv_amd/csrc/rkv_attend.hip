@@ -10,15 +10,17 @@
 //
 // The standalone call copies its slice of page_idx into LDS; several splits per head are combined
 // by k_attend_merge (log-sum-exp form). The fused decode step (k_decode_step) is one kernel:
-//   1. each block scores its share of its head's pages (rkv_approx.hpp) into the workspace and
-//      arrives on a per-head counter; the blocks of a head wait for each other (bounded spin;
-//      the grid never exceeds one block per CU, so all of them are resident at once). Data that
-//      crosses blocks (scores, partial results) moves only through device-coherent stores and
-//      loads ordered by s_waitcnt, so no fence has to write back or invalidate the L2;
-//   2. each block runs the exact block top-k (rkv_select.hpp) on all of its head's page scores
-//      and keeps its slice of the ascending page list;
-//   3. attention over that slice;
-//   4. the last block of the head to finish merges the splits and resets the counters.
+//   1. each block scores its share of its head's pages (rkv_approx.hpp) and publishes them as
+//      epoch-tagged 64-bit words; the attending blocks of the head poll those words until every
+//      tag is current (bounded spin; the grid never exceeds one block per CU, so all of them are
+//      resident at once). Data that crosses blocks moves only through device-coherent loads and
+//      stores, and a tag travels in the same single-copy-atomic word as its value, so no fence
+//      or flag has to order anything;
+//   2. each attending block runs the exact block top-k (rkv_select.hpp) on all of its head's
+//      page scores and keeps its slice of the ascending page list;
+//   3. attention over that slice, published as a tagged partial (max, sum, P.V);
+//   4. every attending block merges a slice of the head's outputs over all partials, and split 0
+//      advances the head's epoch for the next call.
 #include <math.h>
 
 #include <algorithm>
@@ -49,7 +51,7 @@ struct Geo {
 
 template <int D, int G>
 struct AttendShared {
-  int pages[kMaxPagesPerSplit + 1];  // the last slot takes discarded writes
+  int pages[kMaxPagesPerSplit + kWave];  // slots from kMaxPagesPerSplit: discarded writes, per lane
   float m[kWavesPerBlock][G], l[kWavesPerBlock][G];
   float o[kWavesPerBlock][G][D];
 };
@@ -279,115 +281,147 @@ __global__ __launch_bounds__(kThreads) void k_attend_merge(const float* __restri
 
 // ------------------------------------------------------------------------------ fused step
 
-constexpr int kMaxSplit = 64;  // blocks per head in the fused step (one wave polls their flags)
+constexpr int kMaxSplit = 64;  // blocks per head in the fused step
 
+// Cross-block data of the fused step is exchanged as 64-bit words {value bits, epoch}: every
+// block of a head reads the head's epoch word at the start, tags what it publishes with
+// epoch + 1, and readers poll a word until its tag matches, so no flag or counter has to be
+// raised after the data and cleared afterwards. Split 0 stores the new epoch once the merge has
+// seen every split's partial, by which time every block of the head has read the old one.
 struct StepArgs {
   const void* q;
   const void* kmin_t;
   const void* kmax_t;
   const void* k_c;
   const void* v_c;
-  int BH, Hkv, Lc, ps, n_pages, P, r, pps, ppb1, nsplit, nsplit_att, vec;
+  int BH, Hkv, Lc, ps, n_pages, P, r, pps, ppb1, nsplit, nsplit_att, part_cap, vec;
   float scale2;
-  int32_t* chan_idx;  // optional [BH, r]
-  float* scores;      // [BH, P]
-  int32_t* page_idx;  // optional [BH, n_pages]
-  float* part;        // [BH, nsplit_att, G, D+2]
-  unsigned* sync;     // [0] status; arrive flags [BH][kMaxSplit]; done flags [BH][kMaxSplit]
+  int32_t* chan_idx;     // optional [BH, r]
+  float* page_scores;    // optional [BH, P]
+  int32_t* page_idx;     // optional [BH, n_pages]
+  uint64_t* xscores;     // [BH, P] tagged page scores
+  uint64_t* xpart;       // [BH, part_cap, G*D + 2G] tagged partials: o[G*D], M[G], l[G]
+  unsigned* sync;        // [0] status, [16 + bh] epoch of head bh
   void* out;
 };
 
 __device__ __forceinline__ unsigned ld_coherent(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_coherent(const float* p) {
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 template <typename V>
 __device__ __forceinline__ void st_coherent(V* p, V v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t tagged(float v, unsigned epoch) {
+  return ((uint64_t)epoch << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ bool tag_is(uint64_t w, unsigned epoch) {
+  return (unsigned)(w >> 32) == epoch;
+}
+__device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float((unsigned)w); }
 
-// Wave 0 polls flags[lo..hi) (one lane each, one coherent load per poll) until all are set;
-// bounded, on give-up the status word is set. Call from wave 0 only.
-__device__ __forceinline__ void wave_wait_flags(const unsigned* flags, int lo, int hi,
-                                                unsigned* status) {
-  const int lane = threadIdx.x & (kWave - 1);
+// Loads N tagged words (addr(j) for j with use(j)) and polls the stale ones until every tag is
+// `epoch`; bounded, on give-up the status word is set and the stale values are used. Call with
+// the whole wave (the exit is wave-uniform).
+template <int N, typename Addr>
+__device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[N], Addr&& addr,
+                                            unsigned epoch, unsigned* status) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) w[j] = use[j] ? ld_coherent(addr(j)) : 0ull;
   for (int polls = 0;; ++polls) {
-    const bool mine = lane >= lo && lane < hi;
-    const unsigned f = mine ? ld_coherent(flags + lane) : 1u;
-    if (__all(f != 0u)) return;
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < N; ++j) ok = ok && (!use[j] || tag_is(w[j], epoch));
+    if (__all(ok)) return;
     if (polls > kSpinLimit) {
-      if (lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!ok) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (use[j] && !tag_is(w[j], epoch)) w[j] = ld_coherent(addr(j));
   }
 }
+
+template <int D, int G>
+struct MergeShared {
+  float o[G * D + kMaxSplit];  // [split][element of this block's range]
+  float m[kMaxSplit][G];       // max, then the split's weight
+  float l[kMaxSplit][G];
+  float inv[G];
+};
+
+constexpr int kMergePer = 8;  // tagged words a thread loads per round of the merge
 
 template <typename T, int D, int G, int E>
 __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   __shared__ ChannelShared ch;
   // The head's scores are dead once the keys are in registers (block_threshold passes a barrier
-  // before any page-list or attention write), so they share LDS with the attention scratch.
+  // before any page-list or attention write), so they share LDS with the attention scratch; the
+  // merge scratch comes after the attention's last read of it.
   __shared__ union {
     __align__(16) float scores[E * kThreads];
     AttendShared<D, G> att;
+    MergeShared<D, G> mg;
   } u;
   AttendShared<D, G>& sh = u.att;
   float* s_scores = u.scores;
   __shared__ SelectShared<kThreads> sel;
-  __shared__ float s_w[kMaxSplit][G], s_l[kMaxSplit][G];
-  __shared__ float s_inv[G];
-  const int tid = threadIdx.x, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int bh = blockIdx.y, split = blockIdx.x, b = bh / a.Hkv, h = bh % a.Hkv;
   const T* q = static_cast<const T*>(a.q);
-  unsigned* arrive = a.sync + 16 + (size_t)bh * kMaxSplit;
-  unsigned* done = a.sync + 16 + (size_t)a.BH * kMaxSplit + (size_t)bh * kMaxSplit;
+  const bool multi = a.nsplit > 1;
   const bool attends = split < a.nsplit_att;
+  unsigned* epoch_word = a.sync + 16 + bh;
+  unsigned epoch = 0;
+  if (multi) {
+    epoch = ld_coherent(epoch_word) + 1u;
+    if (epoch == 0u) epoch = 1u;  // tag 0 is what a cleared workspace holds
+  }
 
   WaveState<T, D, G> st;  // the queries' loads overlap the channel selection
   if (attends) st.init(q + (size_t)bh * G * D, a.scale2);
 
   // 1. this block's share of the head's approximate page scores
-  select_channels_block<T>(q, b, h, a.Hkv, G, D, a.r, ch);
+  select_channels_block<T, G>(q, b, h, a.Hkv, D, a.r, ch);
   if (a.chan_idx != nullptr && split == 0)
     for (int j = tid; j < a.r; j += kThreads) a.chan_idx[(size_t)bh * a.r + j] = ch.chan[j];
-  float* srow = a.scores + (size_t)bh * a.P;
   {
     const int pb_lo = split * a.ppb1, pb_hi = min(a.P, pb_lo + a.ppb1);
     const size_t sbase = (size_t)bh * D * a.P;
-    // device-coherent stores: the other blocks of the head read them
-    score_page_range<T, true>(static_cast<const T*>(a.kmin_t) + sbase,
-                              static_cast<const T*>(a.kmax_t) + sbase, D, a.P, a.r, pb_lo, pb_hi,
-                              a.vec != 0, ch, srow);
+    const T* kmin_bh = static_cast<const T*>(a.kmin_t) + sbase;
+    const T* kmax_bh = static_cast<const T*>(a.kmax_t) + sbase;
+    float* pso = a.page_scores != nullptr ? a.page_scores + (size_t)bh * a.P : nullptr;
+    uint64_t* xs = a.xscores + (size_t)bh * a.P;
+    auto sink = [&](int p, float v) {
+      if (multi)
+        st_coherent(xs + p, tagged(v, epoch));
+      else
+        s_scores[p] = v;
+      if (pso != nullptr) pso[p] = v;
+    };
+    if (a.vec)
+      score_page_range<T, true>(kmin_bh, kmax_bh, D, a.P, a.r, pb_lo, pb_hi, ch, sink);
+    else
+      score_page_range<T, false>(kmin_bh, kmax_bh, D, a.P, a.r, pb_lo, pb_hi, ch, sink);
   }
-  if (a.nsplit > 1) {
-    // Exchange through device-coherent accesses only: wait until this block's score stores are
-    // complete, raise this block's flag, then wait for every block of the head.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) st_coherent(arrive + split, 1u);
-    if (!attends) return;  // a scoring-only block
-    if (wave == 0) wave_wait_flags(arrive, 0, a.nsplit, a.sync);
-  }
-  __syncthreads();
+  if (!attends) return;  // a scoring-only block
 
   // 2. the head's scores into LDS (coalesced), then the top pages of this block's slice
-  if (a.nsplit > 1) {
-    float v[E];  // every load issued before the first use
+  if (multi) {
+    const uint64_t* xs = a.xscores + (size_t)bh * a.P;
+    uint64_t w[E];
+    bool use[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = j * kThreads + tid;
-      v[j] = i < a.P ? ld_coherent(srow + i) : 0.f;
-    }
+    for (int j = 0; j < E; ++j) use[j] = j * kThreads + tid < a.P;
+    load_tagged<E>(w, use, [&](int j) { return xs + j * kThreads + tid; }, epoch, a.sync);
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = j * kThreads + tid;
-      if (i < a.P) s_scores[i] = v[j];
-    }
-  } else {
-    for (int i = tid; i < a.P; i += kThreads) s_scores[i] = srow[i];
+    for (int j = 0; j < E; ++j)
+      if (use[j]) s_scores[j * kThreads + tid] = tag_value(w[j]);
   }
   __syncthreads();
   const int p_lo = split * a.pps;
@@ -419,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
       block_compact<kThreads, E>(key, nv, thr, need_eq, i0, sel,
                                  [&](uint32_t pos, int idx, bool take) {
         const int p = (int)pos;
-        // branch-free: elements outside the window go to the spare slot
-        sh.pages[(take && p >= w0 && p < w0 + nw) ? p - w0 : kMaxPagesPerSplit] = idx;
+        // branch-free: elements outside the window go to the lane's spare slot
+        sh.pages[(take && p >= w0 && p < w0 + nw) ? p - w0 : kMaxPagesPerSplit + lane] = idx;
         if (write_out && take && p < a.n_pages) pout[p] = idx;
       });
       __syncthreads();
@@ -432,88 +466,85 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   // 3. attention partial of this block
   st.publish(sh);
   __syncthreads();
-  T* out = static_cast<T*>(a.out);
+  T* out = static_cast<T*>(a.out) + (size_t)bh * G * D;
   const int nsa = a.nsplit_att;
-  float* hp = a.part + (size_t)bh * nsa * G * (D + 2);
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, c = idx % D;
-    float M, lsum, o;
-    wave_merge<D, G>(sh, g, c, M, lsum, o);
-    if (nsa == 1) {
-      out[((size_t)bh * G + g) * D + c] = from_f32<T>(lsum > 0.f ? o / lsum : 0.f);
-    } else {
-      float* pp = hp + ((size_t)split * G + g) * (D + 2);
-      st_coherent(pp + c, o);
+  constexpr int kStride = G * D + 2 * G;
+  uint64_t* hp = a.xpart + (size_t)bh * a.part_cap * kStride;
+  if (nsa == 1) {
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      float M, lsum, o;
+      wave_merge<D, G>(sh, idx / D, idx % D, M, lsum, o);
+      out[idx] = from_f32<T>(lsum > 0.f ? o / lsum : 0.f);
+    }
+  } else {
+    uint64_t* mine = hp + (size_t)split * kStride;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D, c = idx % D;
+      float M, lsum, o;
+      wave_merge<D, G>(sh, g, c, M, lsum, o);
+      st_coherent(mine + idx, tagged(o, epoch));
       if (c == 0) {
-        st_coherent(pp + D, M);
-        st_coherent(pp + D + 1, lsum);
+        st_coherent(mine + G * D + g, tagged(M, epoch));
+        st_coherent(mine + G * D + G + g, tagged(lsum, epoch));
       }
     }
   }
+  if (!multi) return;
   if (nsa > 1) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (split != 0) {
-      if (tid == 0) st_coherent(done + split, 1u);
-      return;
-    }
-    // 4. split 0 waits for the other attending blocks, then merges every split
-    if (wave == 0) wave_wait_flags(done, 1, nsa, a.sync);
-    __syncthreads();
-    const size_t stride = (size_t)G * (D + 2);
-    {  // (max, sum) of every split and head into LDS, all loads in flight at once
-      constexpr int kPer = (kMaxSplit * G + kThreads - 1) / kThreads;
-      float mv[kPer], lv[kPer];
+    // 4. this block merges output elements [e0, e0 + ne) over every split
+    const int cpb = (G * D + nsa - 1) / nsa;
+    const int e0 = split * cpb;
+    const int ne = min(cpb, G * D - e0);
+    if (ne <= 0) return;  // (never split 0)
+    const int g0 = e0 / D, ng = (e0 + ne - 1) / D - g0 + 1;
+    const int n_o = nsa * ne, n_all = n_o + 2 * nsa * ng;
+    MergeShared<D, G>& mg = u.mg;
+    __syncthreads();  // the attention scratch is dead from here on
+    for (int base = 0; base < n_all; base += kMergePer * kThreads) {
+      uint64_t w[kMergePer];
+      bool use[kMergePer];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int i = j * kThreads + tid;
-        const bool ok = i < nsa * G;
-        const float* pp = hp + (ok ? (i / G) * stride + (i % G) * (D + 2) : 0);
-        mv[j] = ok ? ld_coherent(pp + D) : 0.f;
-        lv[j] = ok ? ld_coherent(pp + D + 1) : 0.f;
-      }
+      for (int j = 0; j < kMergePer; ++j) use[j] = base + j * kThreads + tid < n_all;
+      auto addr = [&](int j) -> const uint64_t* {
+        const int i = base + j * kThreads + tid;
+        if (i < n_o) return hp + (size_t)(i / ne) * kStride + e0 + i % ne;
+        const int t = i - n_o, which = t / (nsa * ng), rem = t % (nsa * ng);
+        return hp + (size_t)(rem / ng) * kStride + G * D + which * G + g0 + rem % ng;
+      };
+      load_tagged<kMergePer>(w, use, addr, epoch, a.sync);
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int i = j * kThreads + tid;
-        if (i < nsa * G) {
-          s_w[i / G][i % G] = mv[j];
-          s_l[i / G][i % G] = lv[j];
+      for (int j = 0; j < kMergePer; ++j) {
+        const int i = base + j * kThreads + tid;
+        if (!use[j]) continue;
+        const float v = tag_value(w[j]);
+        if (i < n_o) {
+          mg.o[i] = v;
+        } else {
+          const int t = i - n_o, which = t / (nsa * ng), rem = t % (nsa * ng);
+          (which == 0 ? mg.m : mg.l)[rem / ng][rem % ng] = v;
         }
       }
     }
     __syncthreads();
-    if (tid < G) {
-      float M = -INFINITY;
-      for (int s = 0; s < nsa; ++s) M = fmaxf(M, s_w[s][tid]);
-      float lsum = 0.f;
-      for (int s = 0; s < nsa; ++s) {
-        const float ms = s_w[s][tid];
-        const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        lsum = fmaf(s_l[s][tid], wgt, lsum);
-        s_w[s][tid] = wgt;
-      }
-      s_inv[tid] = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (split == 0 && tid == 0) st_coherent(epoch_word, epoch);  // every split has published
+    for (int gg = wave; gg < ng; gg += kWavesPerBlock) {  // lane = split
+      const float ms = lane < nsa ? mg.m[lane][gg] : -INFINITY;
+      const float M = group_max<kWave>(ms);
+      const float wgt = (lane < nsa && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
+      const float lsum = group_sum<kWave>(lane < nsa ? mg.l[lane][gg] * wgt : 0.f);
+      if (lane < nsa) mg.m[lane][gg] = wgt;
+      if (lane == 0) mg.inv[gg] = lsum > 0.f ? 1.f / lsum : 0.f;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int g = idx / D, c = idx % D;
-      const float* pc = hp + (size_t)g * (D + 2) + c;
+    for (int e = tid; e < ne; e += kThreads) {
+      const int gg = (e0 + e) / D - g0;
       float o = 0.f;
-      for (int s0 = 0; s0 < nsa; s0 += 16) {
-        float x[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = s0 + j < nsa ? ld_coherent(pc + (s0 + j) * stride) : 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (s0 + j < nsa) o = fmaf(x[j], s_w[s0 + j][g], o);
-      }
-      out[((size_t)bh * G + g) * D + c] = from_f32<T>(o * s_inv[g]);
+      for (int s = 0; s < nsa; ++s) o = fmaf(mg.o[s * ne + e], mg.m[s][gg], o);
+      out[e0 + e] = from_f32<T>(o * mg.inv[gg]);
     }
-  }
-  // every block of the head has passed its flags: leave them zero for the next call
-  if (a.nsplit > 1 && tid < a.nsplit) {
-    st_coherent(arrive + tid, 0u);
-    st_coherent(done + tid, 0u);
+  } else if (split == 0) {
+    // a single attending block: it has read every score, so every block has read the epoch
+    if (tid == 0) st_coherent(epoch_word, epoch);
   }
 }
 
@@ -629,17 +660,26 @@ StepPlan plan_step_any(int dtype, int D, int BH, int ps, int n_pages, int ncu) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct StepLayout {
-  size_t off_scores, off_part, off_sync, total;
+  size_t off_sync, off_xscores, off_xpart, total;
+  int part_cap;
 };
 
-// Sized for the largest split count any device can get (kTargetBlocks CUs).
-StepLayout step_layout(int B, int Hq, int Hkv, int D, int P, int nsplit_max) {
+// Depends on the shape only (not on n_pages or the device), so one initialised workspace serves
+// every top-k budget of a shape. Partial slots are sized for the largest split count any device
+// can get (kTargetBlocks CUs); a plan with one block per head exchanges nothing.
+StepLayout step_layout(int B, int Hq, int Hkv, int D, int P) {
   const size_t BH = (size_t)B * Hkv;
+  const int G = Hq / Hkv;
   StepLayout lo{};
+  lo.part_cap = max(min(kTargetBlocks / (int)std::min<size_t>(BH, kTargetBlocks), kMaxSplit), 1);
   lo.off_sync = 0;
-  lo.off_scores = align256((16 + 2 * BH * kMaxSplit) * sizeof(unsigned));
-  lo.off_part = align256(lo.off_scores + BH * P * sizeof(float));
-  lo.total = align256(lo.off_part + BH * nsplit_max * (Hq / Hkv) * (D + 2) * sizeof(float));
+  lo.off_xscores = align256((16 + BH) * sizeof(unsigned));
+  if (lo.part_cap == 1) {
+    lo.off_xpart = lo.total = lo.off_xscores;
+    return lo;
+  }
+  lo.off_xpart = align256(lo.off_xscores + BH * P * sizeof(uint64_t));
+  lo.total = align256(lo.off_xpart + BH * lo.part_cap * (size_t)G * (D + 2) * sizeof(uint64_t));
   return lo;
 }
 
@@ -665,11 +705,9 @@ hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
   return D == 64 ? attend_d<bf16_t, 64>(G, a, BH, stream) : attend_d<bf16_t, 128>(G, a, BH, stream);
 }
 
-size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int n_pages,
-                       int dtype) {
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int, int) {
   const int P = (Lc + page_size - 1) / page_size;
-  const StepPlan pl = plan_step_any(dtype, D, B * Hkv, page_size, n_pages, kTargetBlocks);
-  return step_layout(B, Hq, Hkv, D, P, pl.nsplit_att).total;
+  return step_layout(B, Hq, Hkv, D, P).total;
 }
 
 hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream) {
@@ -687,17 +725,17 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
                               void* ws, hipStream_t stream) {
   const int BH = B * Hkv;
   const int P = (Lc + page_size - 1) / page_size;
-  const StepPlan pmax = plan_step_any(dtype, D, BH, page_size, n_pages, kTargetBlocks);
-  const StepPlan pl = plan_step_any(dtype, D, BH, page_size, n_pages, device_cus());
-  const StepLayout lo = step_layout(B, Hq, Hkv, D, P, pmax.nsplit_att);
+  const StepLayout lo = step_layout(B, Hq, Hkv, D, P);
+  StepPlan pl = plan_step_any(dtype, D, BH, page_size, n_pages, device_cus());
+  if (pl.nsplit > lo.part_cap) return hipErrorInvalidValue;  // cannot happen: cap is the maximum
   char* w = static_cast<char*>(ws);
   const int vmax = dtype == 0 ? vec16<float>::n : vec16<bf16_t>::n;
   int ppb1 = (P + pl.nsplit - 1) / pl.nsplit;
   ppb1 = (ppb1 + vmax - 1) / vmax * vmax;
   StepArgs a{q, kmin_t, kmax_t, k_c, v_c, BH, Hkv, Lc, page_size, n_pages, P, r, pl.pps, ppb1,
-             pl.nsplit, pl.nsplit_att, P % vmax == 0, scale * kLog2e, chan_idx,
-             page_scores != nullptr ? page_scores : reinterpret_cast<float*>(w + lo.off_scores),
-             page_idx, reinterpret_cast<float*>(w + lo.off_part),
+             pl.nsplit, pl.nsplit_att, lo.part_cap, P % vmax == 0, scale * kLog2e, chan_idx,
+             page_scores, page_idx, reinterpret_cast<uint64_t*>(w + lo.off_xscores),
+             reinterpret_cast<uint64_t*>(w + lo.off_xpart),
              reinterpret_cast<unsigned*>(w + lo.off_sync), out};
   const int G = Hq / Hkv;
   if (dtype == 0)

@@ -107,47 +107,101 @@ template <int ctrl>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
 }
+template <int ctrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
+}
 
-// Reductions inside groups of `width` consecutive lanes (a power of two <= 64); every lane of
-// the group ends with the result. Within a row the steps are DPP; wider steps are shuffles.
+// gfx950 row swaps (VALU, no LDS round trip). swap16: every lane gets {v of lane l & ~16,
+// v of lane l | 16}; swap32: {v of lane l & ~32, v of lane l | 32}. Both values arrive in the
+// same order in every lane, so a reduction step built on them gives the same bits in all lanes.
+struct LanePair {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ LanePair swap16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ LanePair swap32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {r[0], r[1]};
+}
+
+struct OpSum {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMinU {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct OpMaxU {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+
+template <typename Op>
+__device__ __forceinline__ float xor16_step(float v, Op op) {
+  const LanePair p = swap16(__float_as_uint(v));
+  return op(__uint_as_float(p.lo), __uint_as_float(p.hi));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32_step(float v, Op op) {
+  const LanePair p = swap32(__float_as_uint(v));
+  return op(__uint_as_float(p.lo), __uint_as_float(p.hi));
+}
+
+// Reduction inside groups of `width` consecutive lanes (a power of two <= 64); every lane of the
+// group ends with the result.
+template <int width, typename Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+  if constexpr (width >= 2) v = op(v, dpp<kDppXor1>(v));
+  if constexpr (width >= 4) v = op(v, dpp<kDppXor2>(v));
+  if constexpr (width >= 8) v = op(v, dpp<kDppHalfMirror>(v));
+  if constexpr (width >= 16) v = op(v, dpp<kDppMirror>(v));
+  if constexpr (width >= 32) v = xor16_step(v, op);
+  if constexpr (width >= 64) v = xor32_step(v, op);
+  return v;
+}
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (width >= 2) v += dpp<kDppXor1>(v);
-  if constexpr (width >= 4) v += dpp<kDppXor2>(v);
-  if constexpr (width >= 8) v += dpp<kDppHalfMirror>(v);
-  if constexpr (width >= 16) v += dpp<kDppMirror>(v);
-#pragma unroll
-  for (int o = 16; o < width; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return group_reduce<width>(v, OpSum{});
 }
-
 template <int width>
 __device__ __forceinline__ float group_max(float v) {
-  if constexpr (width >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
-  if constexpr (width >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
-  if constexpr (width >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  if constexpr (width >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-#pragma unroll
-  for (int o = 16; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return group_reduce<width>(v, OpMax{});
 }
 
-// Reduction across the lane groups of a wave: lanes l, l+stride, l+2*stride, ... (stride a power
-// of two < 64) all end with the result.
+// Reduction across the lane groups of a wave: lanes l, l+stride, l+2*stride, ... (stride 8, 16,
+// 32 or 64) all end with the result.
+template <int stride, typename Op>
+__device__ __forceinline__ float across_reduce(float v, Op op) {
+  static_assert(stride == 8 || stride == 16 || stride == 32 || stride == 64, "stride");
+  if constexpr (stride == 8) v = op(v, dpp<kDppRor8>(v));
+  if constexpr (stride <= 16) v = xor16_step(v, op);
+  if constexpr (stride <= 32) v = xor32_step(v, op);
+  return v;
+}
 template <int stride>
 __device__ __forceinline__ float across_sum(float v) {
-  if constexpr (stride == 8) v += dpp<kDppRor8>(v);
-#pragma unroll
-  for (int o = stride < 16 ? 16 : stride; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return across_reduce<stride>(v, OpSum{});
 }
-
 template <int stride>
 __device__ __forceinline__ float across_max(float v) {
-  if constexpr (stride == 8) v = fmaxf(v, dpp<kDppRor8>(v));
-#pragma unroll
-  for (int o = stride < 16 ? 16 : stride; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return across_reduce<stride>(v, OpMax{});
+}
+
+// Whole-wave reduction of a 32-bit unsigned value; every lane ends with the result.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u32<kDppXor1>(v));
+  v = op(v, dpp_u32<kDppXor2>(v));
+  v = op(v, dpp_u32<kDppHalfMirror>(v));
+  v = op(v, dpp_u32<kDppMirror>(v));
+  LanePair p = swap16(v);
+  v = op(p.lo, p.hi);
+  p = swap32(v);
+  return op(p.lo, p.hi);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: row shifts build per-row (16 lane)

@@ -2,14 +2,13 @@
 // Calculating Approximate Attention Scores": select the pages with higher scores).
 //
 // Thread t holds elements [t*E, t*E+E) of the row as order-preserving 32-bit keys. The block
-// first reduces the minimum and maximum key: bits above their highest differing bit are common
-// to every element, so the 8-bit radix digits start right below them (the first digit then
-// spreads over bins instead of piling onto one, which matters for LDS histogram atomics).
-// Each digit pass counts into per-wave histograms (double-buffered, so a pass needs two
-// barriers) and one wave scans the bins from the top to narrow the k-th largest key T; once
-// the bin holding T has at most kSelectCandidates keys, those keys are gathered and T is found
-// by ranking them against each other directly. An ordered compaction then gives every element
-// above T, and the lowest-index elements equal to T, its position in the ascending list.
+// first reduces the minimum and maximum key and counts the keys into kValueBins bins linear in
+// value between them; a scan of the bins from the top finds the bin holding the k-th largest key
+// T, and when that bin holds at most kSelectCandidates keys they are gathered and T is found by
+// ranking them against each other directly. Crowded bins fall back to 8-bit radix passes that
+// start below the bits common to the minimum and maximum, counting into per-wave histograms
+// (double-buffered). An ordered compaction then gives every element above T, and the
+// lowest-index elements equal to T, its position in the ascending list.
 #pragma once
 
 #include "rkv_common.hpp"
@@ -26,39 +25,33 @@ struct SelectShared {
     uint32_t hist[2][NW][256 + kWave];  // bins 256.. take non-matching keys, one per lane (unread)
     uint32_t vbins[kValueBins];
   };
-  uint32_t cand[kSelectCandidates + 1];  // slot kSelectCandidates likewise
-  uint32_t wa[NW];
-  uint32_t wb[NW];
+  __align__(16) uint32_t cand[kSelectCandidates + kWave];  // slots from 256: one spare per lane
+  uint32_t wa[2][NW];  // per-wave partials, two slots so that consecutive scans need no barrier
+  uint32_t wb[2][NW];
   uint32_t digit, above, binc, ncand, thr, need;
 };
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_reduce_u32(v, OpMinU{}); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_reduce_u32(v, OpMaxU{}); }
 
-// Exclusive scan of two counters over the block, plus the totals. Contains two barriers.
+// Exclusive scan of two counters over the block, plus the totals. One barrier; the same slot
+// may be used again only after the block has passed another barrier.
 template <int THREADS>
 __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea, uint32_t& eb,
-                                            uint32_t& ta, uint32_t& tb, SelectShared<THREADS>& sh) {
+                                            uint32_t& ta, uint32_t& tb, SelectShared<THREADS>& sh,
+                                            int slot) {
   constexpr int NW = THREADS / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const uint32_t ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
   if (lane == kWave - 1) {
-    sh.wa[wave] = ia;
-    sh.wb[wave] = ib;
+    sh.wa[slot][wave] = ia;
+    sh.wb[slot][wave] = ib;
   }
   __syncthreads();
   uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const uint32_t va = sh.wa[w], vb = sh.wb[w];
+    const uint32_t va = sh.wa[slot][w], vb = sh.wb[slot][w];
     pa += w < wave ? va : 0u;
     pb += w < wave ? vb : 0u;
     sa += va;
@@ -68,11 +61,58 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea
   eb = pb + ib - b;
   ta = sa;
   tb = sb;
+}
+
+// The keys of one bin (match(key) true for nbin <= kSelectCandidates of them, over the whole
+// block) are gathered into sh.cand, one wave-level slot reservation per wave, and ranked against
+// each other: returns the krem-th largest of them (T) and how many keys equal to T are taken
+// (need). Every thread must call it; three barriers.
+template <int THREADS, int E, typename Match>
+__device__ __forceinline__ void rank_bin(const uint32_t (&key)[E], int nvalid, uint32_t nbin,
+                                         uint32_t krem, Match&& match, uint32_t& T,
+                                         uint32_t& need, SelectShared<THREADS>& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  bool m[E];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    m[e] = e < nvalid && match(key[e]);
+    cnt += m[e] ? 1u : 0u;
+  }
+  const uint32_t incl = wave_inclusive_scan(cnt);
+  uint32_t base = 0;
+  if (lane == kWave - 1 && incl != 0u) base = atomicAdd(&sh.ncand, incl);
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1);
+  uint32_t slot = base + incl - cnt;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {  // branch-free: other keys go to the lane's spare slot
+    sh.cand[m[e] ? slot : (uint32_t)(kSelectCandidates + lane)] = key[e];
+    slot += m[e] ? 1u : 0u;
+  }
   __syncthreads();
+  for (uint32_t t = tid; t < nbin; t += THREADS) {
+    const uint32_t kt = sh.cand[t];
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < nbin; j += 4) {
+      const uint4 c = *reinterpret_cast<const uint4*>(&sh.cand[j]);
+      gt += (c.x > kt) + (j + 1 < nbin && c.y > kt) + (j + 2 < nbin && c.z > kt) +
+            (j + 3 < nbin && c.w > kt);
+      ge += (c.x >= kt) + (j + 1 < nbin && c.y >= kt) + (j + 2 < nbin && c.z >= kt) +
+            (j + 3 < nbin && c.w >= kt);
+    }
+    if (gt < krem && krem <= ge) {  // kt is the krem-th largest key of the bin
+      sh.thr = kt;
+      sh.need = krem - gt;
+    }
+  }
+  __syncthreads();
+  T = sh.thr;
+  need = sh.need;
 }
 
 // Finds T (the k-th largest key) and need_eq (how many keys equal to T are taken), for
-// 1 <= k < number of valid keys. Every thread of the block must call it.
+// 1 <= k < number of valid keys. Every thread of the block must call it. On return the block
+// may run block_compact right away.
 template <int THREADS, int E>
 __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nvalid,
                                                 uint32_t k, uint32_t& T, uint32_t& need_eq,
@@ -90,108 +130,78 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
   if (lane == 0) {
-    sh.wa[wave] = lo;
-    sh.wb[wave] = hi;
+    sh.wa[0][wave] = lo;
+    sh.wb[0][wave] = hi;
   }
-  // both histogram buffers start at zero
-  for (int i = tid; i < 2 * NW * (256 + kWave); i += THREADS) (&sh.hist[0][0][0])[i] = 0u;
+  for (int i = tid; i < kValueBins; i += THREADS) sh.vbins[i] = 0u;
+  if (tid == 0) sh.ncand = 0;
   __syncthreads();
-  lo = sh.wa[0];
-  hi = sh.wb[0];
+  lo = sh.wa[0][0];
+  hi = sh.wb[0][0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
-    lo = min(lo, sh.wa[w]);
-    hi = max(hi, sh.wb[w]);
+    lo = min(lo, sh.wa[0][w]);
+    hi = max(hi, sh.wb[0][w]);
   }
   if (lo == hi) {  // all keys equal
     T = lo;
     need_eq = k;
-    __syncthreads();
     return;
   }
   // Pass over value-linear bins between the block's minimum and maximum: the bin index is a
   // monotone function of the key, so the bin holding the k-th largest key is exact; its keys are
   // then ranked directly. Clustered values (a large bin) fall back to the radix passes below.
-  {
-    const float flo = key_float(lo), fhi = key_float(hi);
-    const float inv = (float)kValueBins / (fhi - flo);
-    if (isfinite(flo) && isfinite(fhi) && isfinite(inv) && inv > 0.f) {
-      auto bin_of = [&](uint32_t kk) {
-        const int b = (int)((key_float(kk) - flo) * inv);
-        return min(max(b, 0), kValueBins - 1);
-      };
-      for (int i = tid; i < kValueBins; i += THREADS) sh.vbins[i] = 0u;
-      if (tid == 0) sh.ncand = 0;
-      __syncthreads();
+  const float flo = key_float(lo), fhi = key_float(hi);
+  const float inv = (float)kValueBins / (fhi - flo);
+  const bool value_pass = isfinite(flo) && isfinite(fhi) && isfinite(inv) && inv > 0.f;
+  if (value_pass) {
+    auto bin_of = [&](uint32_t kk) {
+      const int b = (int)((key_float(kk) - flo) * inv);
+      return min(max(b, 0), kValueBins - 1);
+    };
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (e < nvalid) atomicAdd(&sh.vbins[bin_of(key[e])], 1u);
-      __syncthreads();
-      // thread t owns the kValueBins/THREADS bins just below those of thread t-1 (descending)
-      constexpr int BPT = kValueBins / THREADS;
-      uint32_t c[BPT], local = 0;
+    for (int e = 0; e < E; ++e)
+      if (e < nvalid) atomicAdd(&sh.vbins[bin_of(key[e])], 1u);
+    __syncthreads();
+    // thread t owns the kValueBins/THREADS bins just below those of thread t-1 (descending)
+    constexpr int BPT = kValueBins / THREADS;
+    uint32_t c[BPT], local = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = sh.vbins[kValueBins - 1 - (tid * BPT + j)];
+      local += c[j];
+    }
+    uint32_t excl, unused, tot, unused2;
+    block_scan2<THREADS>(local, 0u, excl, unused, tot, unused2, sh, 0);
+    if (excl < k && k <= excl + local) {
+      uint32_t run = excl;
 #pragma unroll
       for (int j = 0; j < BPT; ++j) {
-        c[j] = sh.vbins[kValueBins - 1 - (tid * BPT + j)];
-        local += c[j];
-      }
-      uint32_t excl, unused, tot, unused2;
-      block_scan2<THREADS>(local, 0u, excl, unused, tot, unused2, sh);
-      if (excl < k && k <= excl + local) {
-        uint32_t run = excl;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-          if (run < k && k <= run + c[j]) {
-            sh.digit = (uint32_t)(kValueBins - 1 - (tid * BPT + j));
-            sh.above = run;
-            sh.binc = c[j];
-          }
-          run += c[j];
+        if (run < k && k <= run + c[j]) {
+          sh.digit = (uint32_t)(kValueBins - 1 - (tid * BPT + j));
+          sh.above = run;
+          sh.binc = c[j];
         }
+        run += c[j];
       }
-      __syncthreads();
-      if (sh.binc <= (uint32_t)kSelectCandidates) {
-        const int bstar = (int)sh.digit;
-        const uint32_t krem = k - sh.above;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (e < nvalid && bin_of(key[e]) == bstar) {
-            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-            sh.cand[slot < (uint32_t)kSelectCandidates ? slot : (uint32_t)kSelectCandidates] = key[e];
-          }
-        }
-        __syncthreads();
-        const uint32_t nc = sh.ncand;
-        for (uint32_t t = tid; t < nc; t += THREADS) {
-          const uint32_t kt = sh.cand[t];
-          uint32_t gt = 0, ge = 0;
-          for (uint32_t j = 0; j < nc; ++j) {
-            const uint32_t kj = sh.cand[j];
-            gt += kj > kt;
-            ge += kj >= kt;
-          }
-          if (gt < krem && krem <= ge) {
-            sh.thr = kt;
-            sh.need = krem - gt;
-          }
-        }
-        __syncthreads();
-        T = sh.thr;
-        need_eq = sh.need;
-        __syncthreads();
-        return;
-      }
-      // a crowded bin: start the radix passes with clean histograms
-      for (int i = tid; i < 2 * NW * (256 + kWave); i += THREADS) (&sh.hist[0][0][0])[i] = 0u;
-      __syncthreads();
+    }
+    __syncthreads();
+    const uint32_t nbin = sh.binc;
+    if (nbin <= (uint32_t)kSelectCandidates) {
+      const int bstar = (int)sh.digit;
+      rank_bin<THREADS, E>(key, nvalid, nbin, k - sh.above,
+                           [&](uint32_t kk) { return bin_of(kk) == bstar; }, T, need_eq, sh);
+      return;
     }
   }
+  // radix passes from clean histograms (they share LDS with the value bins)
+  for (int i = tid; i < 2 * NW * (256 + kWave); i += THREADS) (&sh.hist[0][0][0])[i] = 0u;
+  __syncthreads();
   int bits = 32 - __clz((int)(lo ^ hi));  // low bits that still vary
   uint32_t prefix = bits >= 32 ? 0u : (lo >> bits) << bits;
   uint32_t mask = bits >= 32 ? 0u : ~((1u << bits) - 1u);
   uint32_t krem = k;
   int buf = 0;
-  bool done = false;
   while (bits > 0) {
     const int shift = bits > 8 ? bits - 8 : 0;
     uint32_t* hw = sh.hist[buf][wave];
@@ -215,12 +225,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
         c[j] = x;
         c4 += x;
       }
-      uint32_t incl = c4;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t x = __shfl_up(incl, off, kWave);
-        if (tid >= off) incl += x;
-      }
+      const uint32_t incl = wave_inclusive_scan(c4);
       const uint32_t excl = incl - c4;
       if (excl < krem && krem <= incl) {
         uint32_t run = excl;
@@ -241,46 +246,23 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
     krem -= sh.above;
     bits = shift;
     buf ^= 1;
-    if (bits > 0 && sh.binc <= (uint32_t)kSelectCandidates) {
-      // gather the bin's keys and rank them directly
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (e < nvalid && (key[e] & mask) == prefix) {
-          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-          sh.cand[slot < (uint32_t)kSelectCandidates ? slot : (uint32_t)kSelectCandidates] = key[e];
-        }
-      }
-      __syncthreads();
-      const uint32_t nc = sh.ncand;
-      for (uint32_t t = tid; t < nc; t += THREADS) {
-        const uint32_t kt = sh.cand[t];
-        uint32_t gt = 0, ge = 0;
-        for (uint32_t j = 0; j < nc; ++j) {
-          const uint32_t kj = sh.cand[j];
-          gt += kj > kt;
-          ge += kj >= kt;
-        }
-        if (gt < krem && krem <= ge) {  // kt is the krem-th largest key of the bin
-          sh.thr = kt;
-          sh.need = krem - gt;
-        }
-      }
-      __syncthreads();
-      prefix = sh.thr;
-      krem = sh.need;
-      done = true;
+    const uint32_t nbin = sh.binc;
+    if (bits > 0 && nbin <= (uint32_t)kSelectCandidates) {
+      const uint32_t pm = prefix, mk = mask;
+      rank_bin<THREADS, E>(key, nvalid, nbin, krem, [&](uint32_t kk) { return (kk & mk) == pm; },
+                           prefix, krem, sh);
       break;
     }
   }
-  (void)done;
   T = prefix;
   need_eq = krem;
-  __syncthreads();  // sh.digit / sh.above / sh.wa are rewritten by later uses
+  __syncthreads();  // the last pass's reads of sh.digit / sh.above precede later writes
 }
 
 // Ascending positions of the selected elements. emit(pos, index, selected) is called for every
-// element of the thread (branch-free); pos < k is meaningful only when `selected`. Contains
-// barriers; every thread of the block must call it.
+// element of the thread (branch-free); pos < k is meaningful only when `selected`. One barrier
+// (scan slot 1, whose partials the threshold never touches); every thread of the block must call
+// it, and a second call needs a barrier in between.
 template <int THREADS, int E, typename Emit>
 __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nvalid, uint32_t T,
                                               uint32_t need_eq, int base_index,
@@ -292,7 +274,7 @@ __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nval
     neq += (e < nvalid && key[e] == T);
   }
   uint32_t bg, be, tg, te;
-  block_scan2<THREADS>(ngt, neq, bg, be, tg, te, sh);
+  block_scan2<THREADS>(ngt, neq, bg, be, tg, te, sh, 1);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const bool gt = e < nvalid && key[e] > T;
