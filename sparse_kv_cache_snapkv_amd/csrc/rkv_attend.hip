@@ -323,9 +323,10 @@ __device__ __forceinline__ bool tag_is(uint64_t w, unsigned epoch) {
 }
 __device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float((unsigned)w); }
 
-// Loads N tagged words (addr(j) for j with use(j)) and polls the stale ones until every tag is
-// `epoch`; bounded, on give-up the status word is set and the stale values are used. Call with
-// the whole wave (the exit is wave-uniform).
+// Loads N tagged words (addr(j) for j with use(j)) until every tag is `epoch`. After the first
+// attempt only one stale word per lane is re-read per poll, and the rest only once that one has
+// turned current, so waiting readers add little traffic. Bounded: on give-up the status word is
+// set and the stale values are used. Call with the whole wave (the exit is wave-uniform).
 template <int N, typename Addr>
 __device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[N], Addr&& addr,
                                             unsigned epoch, unsigned* status) {
@@ -340,10 +341,21 @@ __device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[
       if (!ok) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(2);
+    bool probed = false, probe_ok = true;
 #pragma unroll
-    for (int j = 0; j < N; ++j)
-      if (use[j] && !tag_is(w[j], epoch)) w[j] = ld_coherent(addr(j));
+    for (int j = 0; j < N; ++j) {
+      if (!probed && use[j] && !tag_is(w[j], epoch)) {
+        w[j] = ld_coherent(addr(j));
+        probed = true;
+        probe_ok = tag_is(w[j], epoch);
+      }
+    }
+    if (probe_ok) {
+#pragma unroll
+      for (int j = 0; j < N; ++j)
+        if (use[j] && !tag_is(w[j], epoch)) w[j] = ld_coherent(addr(j));
+    }
   }
 }
 
@@ -450,7 +462,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
       const int nw = min(kMaxPagesPerSplit, max(p_hi - w0, 0));
       const bool write_out = pout != nullptr && w0 == p_lo;
       __syncthreads();
-      block_compact<kThreads, E>(key, nv, thr, need_eq, i0, sel,
+      const uint32_t wlo = write_out ? 0u : (uint32_t)w0;
+      const uint32_t whi = write_out ? (uint32_t)a.n_pages : (uint32_t)(w0 + nw);
+      block_compact<kThreads, E>(key, nv, thr, need_eq, i0, wlo, whi, sel,
                                  [&](uint32_t pos, int idx, bool take) {
         const int p = (int)pos;
         // branch-free: elements outside the window go to the lane's spare slot

@@ -63,10 +63,10 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea
   tb = sb;
 }
 
-// The keys of one bin (match(key) true for nbin <= kSelectCandidates of them, over the whole
-// block) are gathered into sh.cand, one wave-level slot reservation per wave, and ranked against
-// each other: returns the krem-th largest of them (T) and how many keys equal to T are taken
-// (need). Every thread must call it; three barriers.
+// The keys of one bin (match(e) true for element e of nbin <= kSelectCandidates keys over the
+// whole block) are gathered into sh.cand, one wave-level slot reservation per wave, and ranked
+// against each other: returns the krem-th largest of them (T) and how many keys equal to T are
+// taken (need). Every thread must call it; two barriers.
 template <int THREADS, int E, typename Match>
 __device__ __forceinline__ void rank_bin(const uint32_t (&key)[E], int nvalid, uint32_t nbin,
                                          uint32_t krem, Match&& match, uint32_t& T,
@@ -76,7 +76,7 @@ __device__ __forceinline__ void rank_bin(const uint32_t (&key)[E], int nvalid, u
   uint32_t cnt = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    m[e] = e < nvalid && match(key[e]);
+    m[e] = e < nvalid && match(e);
     cnt += m[e] ? 1u : 0u;
   }
   const uint32_t incl = wave_inclusive_scan(cnt);
@@ -155,13 +155,12 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
   const float inv = (float)kValueBins / (fhi - flo);
   const bool value_pass = isfinite(flo) && isfinite(fhi) && isfinite(inv) && inv > 0.f;
   if (value_pass) {
-    auto bin_of = [&](uint32_t kk) {
-      const int b = (int)((key_float(kk) - flo) * inv);
-      return min(max(b, 0), kValueBins - 1);
-    };
+    int bin[E];  // a monotone function of the key, computed once
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (e < nvalid) atomicAdd(&sh.vbins[bin_of(key[e])], 1u);
+    for (int e = 0; e < E; ++e) {
+      bin[e] = min(max((int)((key_float(key[e]) - flo) * inv), 0), kValueBins - 1);
+      if (e < nvalid) atomicAdd(&sh.vbins[bin[e]], 1u);
+    }
     __syncthreads();
     // thread t owns the kValueBins/THREADS bins just below those of thread t-1 (descending)
     constexpr int BPT = kValueBins / THREADS;
@@ -190,7 +189,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
     if (nbin <= (uint32_t)kSelectCandidates) {
       const int bstar = (int)sh.digit;
       rank_bin<THREADS, E>(key, nvalid, nbin, k - sh.above,
-                           [&](uint32_t kk) { return bin_of(kk) == bstar; }, T, need_eq, sh);
+                           [&](int e) { return bin[e] == bstar; }, T, need_eq, sh);
       return;
     }
   }
@@ -249,7 +248,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
     const uint32_t nbin = sh.binc;
     if (bits > 0 && nbin <= (uint32_t)kSelectCandidates) {
       const uint32_t pm = prefix, mk = mask;
-      rank_bin<THREADS, E>(key, nvalid, nbin, krem, [&](uint32_t kk) { return (kk & mk) == pm; },
+      rank_bin<THREADS, E>(key, nvalid, nbin, krem, [&](int e) { return (key[e] & mk) == pm; },
                            prefix, krem, sh);
       break;
     }
@@ -260,13 +259,15 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
 }
 
 // Ascending positions of the selected elements. emit(pos, index, selected) is called for every
-// element of the thread (branch-free); pos < k is meaningful only when `selected`. One barrier
-// (scan slot 1, whose partials the threshold never touches); every thread of the block must call
-// it, and a second call needs a barrier in between.
+// element of a thread whose selected elements (which take consecutive positions) reach into
+// [win_lo, win_hi), and for no element of the other threads; pos is meaningful only when
+// `selected`. One barrier (scan slot 1, whose partials the threshold never touches); every
+// thread of the block must call it, and a second call needs a barrier in between.
 template <int THREADS, int E, typename Emit>
 __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nvalid, uint32_t T,
-                                              uint32_t need_eq, int base_index,
-                                              SelectShared<THREADS>& sh, Emit&& emit) {
+                                              uint32_t need_eq, int base_index, uint32_t win_lo,
+                                              uint32_t win_hi, SelectShared<THREADS>& sh,
+                                              Emit&& emit) {
   uint32_t ngt = 0, neq = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -275,6 +276,9 @@ __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nval
   }
   uint32_t bg, be, tg, te;
   block_scan2<THREADS>(ngt, neq, bg, be, tg, te, sh, 1);
+  const uint32_t first = bg + min(be, need_eq);
+  const uint32_t ntake = ngt + (be < need_eq ? min(neq, need_eq - be) : 0u);
+  if (ntake == 0u || first >= win_hi || first + ntake <= win_lo) return;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const bool gt = e < nvalid && key[e] > T;

@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk_block(const float* __res
   const int nv = load_keys<E>(row, n, i0, key);
   uint32_t T, need_eq;
   block_threshold<kBlockThreads, E>(key, nv, (uint32_t)k, T, need_eq, sh);
-  block_compact<kBlockThreads, E>(key, nv, T, need_eq, i0, sh,
+  block_compact<kBlockThreads, E>(key, nv, T, need_eq, i0, 0u, (uint32_t)k, sh,
                                   [&](uint32_t pos, int idx, bool take) {
                                     if (take && pos < (uint32_t)k) o[pos] = idx;
                                   });
