@@ -175,16 +175,19 @@ int rkv_sparse_attend_decode(const void* q, const void* k_c, const void* v_c,
  *
  * q, kmin_t, kmax_t, k_c, v_c, out as in the three calls; n_pages = pages to select (1..P).
  * chan_idx    [B, Hkv, r]       int32 out, may be NULL
- * page_scores [B, Hkv, P]       float out, may be NULL (then kept in the workspace)
+ * page_scores [B, Hkv, P]       float out, may be NULL
  * page_idx    [B, Hkv, n_pages] int32 out, may be NULL: the selected pages, ascending
  * Requires P = ceil(Lc/page_size) <= 8192 and the limits of the three calls.
- * ws          rkv_hybrid_decode_workspace_bytes(...) bytes, prepared ONCE after allocation by
- *             rkv_hybrid_decode_workspace_init (it holds per-head counters that every call
- *             leaves zero). The blocks of a head synchronise through those counters with a
- *             bounded wait; the grid never exceeds one block per CU. If a wait ever gave up
- *             (only possible when other work occupies the GPU's CUs at the same time), the
- *             uint32 at byte offset 0 of ws becomes nonzero and stays so: that call's output is
- *             not valid. Calls that overlap in time must not share a workspace.
+ * ws          rkv_hybrid_decode_workspace_bytes(...) bytes (its size depends on the shape B,
+ *             Hq, Hkv, Lc, D, page_size and dtype, not on n_pages), zero-filled ONCE by
+ *             rkv_hybrid_decode_workspace_init before its first use, and again before it is used
+ *             for a different shape. The blocks of a head exchange scores and partial results
+ *             through it as 64-bit words tagged with a per-head call counter that the workspace
+ *             also holds, so no call has to clear anything for the next one; readers wait for
+ *             current tags with a bounded wait, and the grid never exceeds one block per CU. If
+ *             a wait ever gave up (only possible when other work occupies the GPU's CUs at the
+ *             same time), the uint32 at byte offset 0 of ws becomes nonzero and stays so: that
+ *             call's output is not valid. Calls that overlap in time must not share a workspace.
  * ------------------------------------------------------------------------------------------ */
 int rkv_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size,
                                       int n_pages, int dtype, size_t* bytes);
