@@ -24,11 +24,11 @@ struct ChannelShared {
 // value for non-negative floats, above 127 - c, so equal sums rank the lower channel higher);
 // thread t counts the keys of channels [64*(t/128), 64*(t/128) + 64) above channel t % 128's
 // key, and the two halves add up to its rank. Wave 0 then places the channels of rank < r in
-// ascending channel order by ballot prefix counts. Three barriers; the block must have at least
-// 256 threads and every thread must call it.
+// ascending channel order by ballot prefix counts. The block must have at least 256 threads and
+// every thread must call both phases; phase 1 ends with a barrier, phase 2 contains two.
 template <typename T, int G>
-__device__ __forceinline__ void select_channels_block(const T* __restrict__ q, int b, int h,
-                                                      int Hkv, int D, int r, ChannelShared& sh) {
+__device__ __forceinline__ void select_channels_phase1(const T* __restrict__ q, int b, int h,
+                                                       int Hkv, int D, ChannelShared& sh) {
   const int tid = threadIdx.x;
   if (tid < kApproxMaxD) {
     const int c = tid;
@@ -47,6 +47,10 @@ __device__ __forceinline__ void select_channels_block(const T* __restrict__ q, i
     sh.qb[c] = sq;
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShared& sh) {
+  const int tid = threadIdx.x;
   if (tid < 2 * kApproxMaxD) {
     const int c = tid % kApproxMaxD, half = tid / kApproxMaxD;
     const uint64_t kc = sh.key[c];
@@ -78,6 +82,13 @@ __device__ __forceinline__ void select_channels_block(const T* __restrict__ q, i
     }
   }
   __syncthreads();
+}
+
+template <typename T, int G>
+__device__ __forceinline__ void select_channels_block(const T* __restrict__ q, int b, int h,
+                                                      int Hkv, int D, int r, ChannelShared& sh) {
+  select_channels_phase1<T, G>(q, b, h, Hkv, D, sh);
+  select_channels_phase2(D, r, sh);
 }
 
 // Channel partition of the page-score sum: group g (of 16) sums chosen channels g, g+16, g+32,
