@@ -35,10 +35,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct EvictLayout {
   int GW, GWp, nchunk1, nsub1, nchunk2, nsub2, nprefix;
-  size_t off_stats, off_lse, off_colsum, off_pooled, total;
+  size_t off_stats, off_lse, off_colsum, off_pooled, off_topk, total;
 };
 
-EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int dtype) {
+EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int keep, int dtype) {
   EvictLayout lo{};
   const int BH = B * Hkv;
   lo.GW = (Hq / Hkv) * W;
@@ -68,6 +68,8 @@ EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int dtype) {
   off = align256(off + (size_t)BH * (lo.nprefix > 0 ? lo.nprefix : 1) * sizeof(float));
   lo.off_pooled = off;
   off = align256(off + (size_t)BH * (lo.nprefix > 0 ? lo.nprefix : 1) * sizeof(float));
+  lo.off_topk = off;
+  off = align256(off + topk_ws_bytes(BH, lo.nprefix > 0 ? lo.nprefix : 1, keep - W));
   lo.total = off;
   return lo;
 }
@@ -467,7 +469,7 @@ hipError_t scores_f32(const void* q_win, const void* k, int BH, int L, int W,
 size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype) {
   (void)D;
   if (keep >= L) return 0;
-  return layout_for(B, Hq, Hkv, L, W, dtype).total;
+  return layout_for(B, Hq, Hkv, L, W, keep, dtype).total;
 }
 
 hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, int Hq, int Hkv,
@@ -477,7 +479,7 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
   const int BH = B * Hkv;
   if (keep >= L)
     return gather_any(dtype, D, k, v, BH, L, W, L, 1, kept_idx, k_out, v_out, stream);
-  const EvictLayout lo = layout_for(B, Hq, Hkv, L, W, dtype);
+  const EvictLayout lo = layout_for(B, Hq, Hkv, L, W, keep, dtype);
   char* w = static_cast<char*>(ws);
   const float scale2 = scale * kLog2e;
   hipError_t e;
@@ -494,7 +496,8 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
   hipLaunchKernelGGL(k_pool, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, stream,
                      colsum, n, pool_kernel, pool_type, pooled);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_topk(pooled, BH, n, keep - W, kept_idx, keep, nullptr, stream)) != hipSuccess)
+  if ((e = launch_topk(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk, stream)) !=
+      hipSuccess)
     return e;
   return gather_any(dtype, D, k, v, BH, L, W, keep, 0, kept_idx, k_out, v_out, stream);
 }

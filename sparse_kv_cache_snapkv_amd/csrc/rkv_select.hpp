@@ -263,11 +263,14 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
 // [win_lo, win_hi), and for no element of the other threads; pos is meaningful only when
 // `selected`. One barrier (scan slot 1, whose partials the threshold never touches); every
 // thread of the block must call it, and a second call needs a barrier in between.
+// gt_base / eq_base: elements above / equal to T that precede this block's elements in the row
+// (when a row is spread over several blocks).
 template <int THREADS, int E, typename Emit>
 __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nvalid, uint32_t T,
                                               uint32_t need_eq, int base_index, uint32_t win_lo,
                                               uint32_t win_hi, SelectShared<THREADS>& sh,
-                                              Emit&& emit) {
+                                              Emit&& emit, uint32_t gt_base = 0,
+                                              uint32_t eq_base = 0) {
   uint32_t ngt = 0, neq = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -276,6 +279,8 @@ __device__ __forceinline__ void block_compact(const uint32_t (&key)[E], int nval
   }
   uint32_t bg, be, tg, te;
   block_scan2<THREADS>(ngt, neq, bg, be, tg, te, sh, 1);
+  bg += gt_base;
+  be += eq_base;
   const uint32_t first = bg + min(be, need_eq);
   const uint32_t ntake = ngt + (be < need_eq ? min(neq, need_eq - be) : 0u);
   if (ntake == 0u || first >= win_hi || first + ntake <= win_lo) return;

@@ -4,8 +4,14 @@
 //
 // Rows of up to 8192 elements (page scores of a decode step): one 256-thread block per row holds
 // the row in registers and runs the block select of rkv_select.hpp. Longer rows (prompt token
-// scores): one 1024-thread block per row, four 8-bit digit passes over LDS histograms that
-// re-read the row each pass (it is L2-resident after the first), then an ordered compaction.
+// scores) are spread over blocks of 4096 elements each, in six short launches: clear the
+// row histograms; three digit levels (bits 31..21, 20..10, 9..0 of the keys), each block
+// counting the digits of its keys that match the prefix found so far into the row's global
+// histogram (every block of the next launch re-derives that prefix from it); a per-block count
+// of the keys above and equal to the threshold; and the ordered write, where each block offsets
+// its block-level compaction by the counts of the blocks before it.
+#include <algorithm>
+
 #include "rkv_common.hpp"
 #include "rkv_launch.hpp"
 #include "rkv_select.hpp"
@@ -13,203 +19,6 @@
 namespace rkv {
 
 namespace {
-
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kTile = kThreads * 4;  // elements per tile: 4 consecutive per thread
-
-struct TopkShared {
-  uint32_t hist[256];
-  uint32_t wave_a[kWaves];
-  uint32_t wave_b[kWaves];
-  uint32_t digit;
-  uint32_t above;
-};
-
-// Exclusive block scan of two counters; also returns the block totals.
-__device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea, uint32_t& eb,
-                                            uint32_t& ta, uint32_t& tb, TopkShared& sh) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  uint32_t ia = a, ib = b;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t xa = __shfl_up(ia, o, kWave);
-    const uint32_t xb = __shfl_up(ib, o, kWave);
-    if (lane >= o) {
-      ia += xa;
-      ib += xb;
-    }
-  }
-  if (lane == kWave - 1) {
-    sh.wave_a[wave] = ia;
-    sh.wave_b[wave] = ib;
-  }
-  __syncthreads();
-  uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t va = sh.wave_a[w], vb = sh.wave_b[w];
-    if (w < wave) {
-      pa += va;
-      pb += vb;
-    }
-    sa += va;
-    sb += vb;
-  }
-  ea = pa + ia - a;
-  eb = pb + ib - b;
-  ta = sa;
-  tb = sb;
-  __syncthreads();
-}
-
-__device__ __forceinline__ void load4(const float* __restrict__ s, int n, int i0, uint32_t (&key)[4],
-                                      bool (&ok)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = i0 + e;
-    ok[e] = i < n;
-    key[e] = ok[e] ? order_key(s[i]) : 0u;
-  }
-}
-
-template <int R>
-__global__ __launch_bounds__(kThreads) void k_topk(const float* __restrict__ scores, int n, int k,
-                                                   int32_t* __restrict__ out, int out_stride) {
-  __shared__ TopkShared sh;
-  const int tid = threadIdx.x;
-  const float* s = scores + (size_t)blockIdx.x * n;
-  int32_t* o = out + (size_t)blockIdx.x * out_stride;
-  if (k >= n) {
-    for (int i = tid; i < n; i += kThreads) o[i] = i;
-    return;
-  }
-  if (k <= 0) return;
-  const int ntiles = (n + kTile - 1) / kTile;
-
-  uint32_t rkey[R > 0 ? R : 1][4];
-  bool rok[R > 0 ? R : 1][4];
-  if constexpr (R > 0) {
-#pragma unroll
-    for (int t = 0; t < R; ++t) load4(s, n, (t * kThreads + tid) * 4, rkey[t], rok[t]);
-  }
-
-  uint32_t prefix = 0, mask = 0;
-  uint32_t krem = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) sh.hist[tid] = 0;
-    __syncthreads();
-    auto count4 = [&](const uint32_t (&key)[4], const bool (&ok)[4]) {
-      // merge equal digits of the thread's four elements before touching LDS
-      uint32_t d[4];
-      uint32_t c[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool m = ok[e] && ((key[e] & mask) == prefix);
-        d[e] = (key[e] >> shift) & 255u;
-        c[e] = m ? 1u : 0u;
-      }
-#pragma unroll
-      for (int e = 1; e < 4; ++e) {
-#pragma unroll
-        for (int f = 0; f < e; ++f) {
-          if (c[e] && c[f] && d[f] == d[e]) {
-            c[f] += c[e];
-            c[e] = 0;
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (c[e]) atomicAdd(&sh.hist[d[e]], c[e]);
-    };
-    if constexpr (R > 0) {
-#pragma unroll
-      for (int t = 0; t < R; ++t) count4(rkey[t], rok[t]);
-    } else {
-      for (int t = 0; t < ntiles; ++t) {
-        uint32_t key[4];
-        bool ok[4];
-        load4(s, n, (t * kThreads + tid) * 4, key, ok);
-        count4(key, ok);
-      }
-    }
-    __syncthreads();
-    if (tid < kWave) {
-      // lane l owns digits 255-4l .. 252-4l (descending); find the digit holding the krem-th key
-      uint32_t c4 = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c4 += sh.hist[255 - 4 * tid - j];
-      uint32_t incl = c4;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t x = __shfl_up(incl, off, kWave);
-        if (tid >= off) incl += x;
-      }
-      const uint32_t excl = incl - c4;
-      if (excl < krem && krem <= incl) {
-        uint32_t run = excl;
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t dgt = 255 - 4 * tid - j;
-          const uint32_t c = sh.hist[dgt];
-          if (run + c >= krem) {
-            sh.digit = dgt;
-            sh.above = run;
-            break;
-          }
-          run += c;
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= sh.digit << shift;
-    mask |= 255u << shift;
-    krem -= sh.above;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const uint32_t need_eq = krem;  // elements equal to T that are taken (lowest indices first)
-
-  uint32_t carry_gt = 0, carry_eq = 0;
-  auto emit4 = [&](const uint32_t (&key)[4], const bool (&ok)[4], int i0) {
-    uint32_t ngt = 0, neq = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ngt += (ok[e] && key[e] > T);
-      neq += (ok[e] && key[e] == T);
-    }
-    uint32_t egt, eeq, tgt, teq;
-    block_scan2(ngt, neq, egt, eeq, tgt, teq, sh);
-    uint32_t bg = carry_gt + egt, be = carry_eq + eeq;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!ok[e]) continue;
-      if (key[e] > T) {
-        const uint32_t pos = bg + (be < need_eq ? be : need_eq);
-        if (pos < (uint32_t)k) o[pos] = i0 + e;
-        ++bg;
-      } else if (key[e] == T) {
-        if (be < need_eq && bg + be < (uint32_t)k) o[bg + be] = i0 + e;
-        ++be;
-      }
-    }
-    carry_gt += tgt;
-    carry_eq += teq;
-  };
-  if constexpr (R > 0) {
-#pragma unroll
-    for (int t = 0; t < R; ++t) emit4(rkey[t], rok[t], (t * kThreads + tid) * 4);
-  } else {
-    for (int t = 0; t < ntiles; ++t) {
-      uint32_t key[4];
-      bool ok[4];
-      const int i0 = (t * kThreads + tid) * 4;
-      load4(s, n, i0, key, ok);
-      emit4(key, ok, i0);
-    }
-  }
-}
 
 constexpr int kBlockThreads = 256;
 
@@ -237,21 +46,243 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk_block(const float* __res
                                   });
 }
 
+// ------------------------------------------------------------------------------ long rows
+
+constexpr int kLongPer = 16;                          // keys per thread
+constexpr int kLongChunk = kBlockThreads * kLongPer;  // keys per block
+constexpr int kLevels = 3;         // digit levels: key bits 31..21, 20..10, 9..0
+constexpr int kHistStride = 2048;  // words per level and row
+__host__ __device__ constexpr int level_shift(int lev) { return lev == 0 ? 21 : (lev == 1 ? 10 : 0); }
+__host__ __device__ constexpr int level_bits(int lev) { return lev == 2 ? 10 : 11; }
+__host__ __device__ constexpr int level_bins(int lev) { return 1 << level_bits(lev); }
+
+struct LongLayout {
+  int nblk;
+  size_t off_hist, off_cnt, off_thr, total;
+};
+
+LongLayout long_layout(int rows, int n) {
+  LongLayout lo{};
+  lo.nblk = (n + kLongChunk - 1) / kLongChunk;
+  lo.off_hist = 0;
+  lo.off_cnt = lo.off_hist + (size_t)rows * kLevels * kHistStride * sizeof(uint32_t);
+  lo.off_cnt = (lo.off_cnt + 255) & ~(size_t)255;
+  lo.off_thr = lo.off_cnt + (size_t)rows * lo.nblk * 2 * sizeof(uint32_t);
+  lo.off_thr = (lo.off_thr + 255) & ~(size_t)255;
+  lo.total = lo.off_thr + (size_t)rows * 2 * sizeof(uint32_t);
+  lo.total = (lo.total + 255) & ~(size_t)255;
+  return lo;
+}
+
+bool long_path(int n, int k) { return n > 32 * kBlockThreads && k > 0 && k < n; }
+
+__global__ void k_long_zero(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The digit of level `lev` holding the krem-th largest key of the keys counted in `hist` (the
+// row's histogram of that level, finished by an earlier launch), and how many counted keys lie in
+// higher digits. Every thread must call it; two barriers.
+__device__ __forceinline__ void find_digit(const uint32_t* __restrict__ hist, int nbins,
+                                           uint32_t krem, uint32_t& digit, uint32_t& above,
+                                           SelectShared<kBlockThreads>& sh) {
+  const int tid = threadIdx.x;
+  const int bpt = nbins / kBlockThreads;  // 8 or 4 digits per thread, descending
+  uint32_t c[8], local = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[j] = j < bpt ? hist[nbins - 1 - (tid * bpt + j)] : 0u;
+    local += c[j];
+  }
+  uint32_t excl, unused, tot, unused2;
+  block_scan2<kBlockThreads>(local, 0u, excl, unused, tot, unused2, sh, 0);
+  if (excl < krem && krem <= excl + local) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < bpt && run < krem && krem <= run + c[j]) {
+        sh.digit = (uint32_t)(nbins - 1 - (tid * bpt + j));
+        sh.above = run;
+      }
+      run += c[j];
+    }
+  }
+  __syncthreads();
+  digit = sh.digit;
+  above = sh.above;
+  __syncthreads();  // sh.digit / the scan partials are rewritten by the next call
+}
+
+// Re-derives the prefix (the key bits above level `upto`) and the rank still to place within it.
+__device__ __forceinline__ void long_prefix(const uint32_t* __restrict__ hist_row, int upto,
+                                            uint32_t k, uint32_t& prefix, uint32_t& krem,
+                                            SelectShared<kBlockThreads>& sh) {
+  prefix = 0u;
+  krem = k;
+  for (int lev = 0; lev < upto; ++lev) {
+    uint32_t d, above;
+    find_digit(hist_row + lev * kHistStride, level_bins(lev), krem, d, above, sh);
+    prefix |= d << level_shift(lev);
+    krem -= above;
+  }
+}
+
+template <int LEVEL>
+__global__ __launch_bounds__(kBlockThreads) void k_long_hist(const float* __restrict__ scores,
+                                                            int n, int k,
+                                                            uint32_t* __restrict__ hist) {
+  __shared__ SelectShared<kBlockThreads> sh;
+  __shared__ uint32_t lh[kHistStride];
+  const int tid = threadIdx.x, row = blockIdx.y;
+  uint32_t* hist_row = hist + (size_t)row * kLevels * kHistStride;
+  uint32_t prefix, krem;
+  long_prefix(hist_row, LEVEL, (uint32_t)k, prefix, krem, sh);
+  constexpr int shift = level_shift(LEVEL), nbins = level_bins(LEVEL);
+  constexpr int top = shift + level_bits(LEVEL);  // the digit's highest bit + 1
+  for (int i = tid; i < nbins; i += kBlockThreads) lh[i] = 0u;
+  __syncthreads();
+  const float* s = scores + (size_t)row * n + (size_t)blockIdx.x * kLongChunk;
+  const int nv = min(kLongChunk, n - (int)blockIdx.x * kLongChunk);
+  float v[kLongPer];
+#pragma unroll
+  for (int j = 0; j < kLongPer; ++j) {
+    v[j] = 0.f;
+    if (j * kBlockThreads + tid < nv) v[j] = s[j * kBlockThreads + tid];
+  }
+#pragma unroll
+  for (int j = 0; j < kLongPer; ++j) {
+    const uint32_t key = order_key(v[j]);
+    const bool match = j * kBlockThreads + tid < nv &&
+                       (top >= 32 || (key >> top) == (prefix >> top));
+    if (match) atomicAdd(&lh[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+  }
+  __syncthreads();
+  uint32_t* hl = hist_row + LEVEL * kHistStride;
+  for (int i = tid; i < nbins; i += kBlockThreads)
+    if (lh[i] != 0u) atomicAdd(&hl[i], lh[i]);
+}
+
+// Threshold key T and the number of keys equal to T to take; per-block counts of the keys above
+// and equal to T. Block 0 of each row also stores (T, need) for the write launch.
+__global__ __launch_bounds__(kBlockThreads) void k_long_count(const float* __restrict__ scores,
+                                                             int n, int k,
+                                                             const uint32_t* __restrict__ hist,
+                                                             uint32_t* __restrict__ cnt,
+                                                             uint32_t* __restrict__ thr) {
+  __shared__ SelectShared<kBlockThreads> sh;
+  const int tid = threadIdx.x, row = blockIdx.y, nblk = gridDim.x;
+  uint32_t T, need;
+  long_prefix(hist + (size_t)row * kLevels * kHistStride, kLevels, (uint32_t)k, T, need, sh);
+  const float* s = scores + (size_t)row * n + (size_t)blockIdx.x * kLongChunk;
+  const int nv = min(kLongChunk, n - (int)blockIdx.x * kLongChunk);
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kLongPer; ++j) {
+    const int i = j * kBlockThreads + tid;
+    float x = 0.f;
+    if (i < nv) x = s[i];
+    const uint32_t key = order_key(x);
+    gt += (i < nv && key > T) ? 1u : 0u;
+    eq += (i < nv && key == T) ? 1u : 0u;
+  }
+  uint32_t e0, e1, tg, te;
+  block_scan2<kBlockThreads>(gt, eq, e0, e1, tg, te, sh, 1);
+  if (tid == 0) {
+    cnt[((size_t)row * nblk + blockIdx.x) * 2] = tg;
+    cnt[((size_t)row * nblk + blockIdx.x) * 2 + 1] = te;
+    if (blockIdx.x == 0) {
+      thr[(size_t)row * 2] = T;
+      thr[(size_t)row * 2 + 1] = need;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_long_write(const float* __restrict__ scores,
+                                                             int n, int k,
+                                                             const uint32_t* __restrict__ cnt,
+                                                             const uint32_t* __restrict__ thr,
+                                                             int32_t* __restrict__ out,
+                                                             int out_stride) {
+  __shared__ SelectShared<kBlockThreads> sh;
+  const int tid = threadIdx.x, row = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+  const uint32_t T = thr[(size_t)row * 2], need = thr[(size_t)row * 2 + 1];
+  // keys above / equal to T in the blocks before this one
+  uint32_t bgt = 0, beq = 0;
+  for (int b = tid; b < blk; b += kBlockThreads) {
+    bgt += cnt[((size_t)row * nblk + b) * 2];
+    beq += cnt[((size_t)row * nblk + b) * 2 + 1];
+  }
+  uint32_t e0, e1, gt_base, eq_base;
+  block_scan2<kBlockThreads>(bgt, beq, e0, e1, gt_base, eq_base, sh, 0);
+  const int base = blk * kLongChunk;
+  const float* s = scores + (size_t)row * n + base;
+  const int nv_blk = min(kLongChunk, n - base);
+  uint32_t key[kLongPer];
+  const int i0 = tid * kLongPer;
+  const int nv = load_keys<kLongPer>(s, nv_blk, i0, key);
+  int32_t* o = out + (size_t)row * out_stride;
+  block_compact<kBlockThreads, kLongPer>(
+      key, nv, T, need, base + i0, 0u, (uint32_t)k, sh,
+      [&](uint32_t pos, int idx, bool take) {
+        if (take && pos < (uint32_t)k) o[pos] = idx;
+      },
+      gt_base, eq_base);
+}
+
+__global__ void k_fill_identity(int32_t* out, int n, int out_stride) {
+  int32_t* o = out + (size_t)blockIdx.y * out_stride;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) o[i] = i;
+}
+
 }  // namespace
 
-size_t topk_ws_bytes(int, int, int) { return 0; }
+size_t topk_ws_bytes(int rows, int n, int k) {
+  return long_path(n, k) ? long_layout(rows, n).total : 0;
+}
 
 hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out, int out_stride,
-                       void*, hipStream_t stream) {
+                       void* ws, hipStream_t stream) {
   dim3 grid(rows);
-  if (n <= 16 * kBlockThreads)
+  if (n <= 16 * kBlockThreads) {
     hipLaunchKernelGGL(k_topk_block<16>, grid, dim3(kBlockThreads), 0, stream, scores, n, k, out,
                        out_stride);
-  else if (n <= 32 * kBlockThreads)
+    return hipGetLastError();
+  }
+  if (n <= 32 * kBlockThreads) {
     hipLaunchKernelGGL(k_topk_block<32>, grid, dim3(kBlockThreads), 0, stream, scores, n, k, out,
                        out_stride);
-  else
-    hipLaunchKernelGGL(k_topk<0>, grid, dim3(kThreads), 0, stream, scores, n, k, out, out_stride);
+    return hipGetLastError();
+  }
+  if (k <= 0) return hipSuccess;
+  if (k >= n) {
+    hipLaunchKernelGGL(k_fill_identity, dim3((n + kBlockThreads - 1) / kBlockThreads, rows),
+                       dim3(kBlockThreads), 0, stream, out, n, out_stride);
+    return hipGetLastError();
+  }
+  const LongLayout lo = long_layout(rows, n);
+  char* w = static_cast<char*>(ws);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(w + lo.off_hist);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + lo.off_cnt);
+  uint32_t* thr = reinterpret_cast<uint32_t*>(w + lo.off_thr);
+  const size_t nhist = (size_t)rows * kLevels * kHistStride;
+  hipLaunchKernelGGL(k_long_zero, dim3((unsigned)std::min<size_t>((nhist + 255) / 256, 1024)),
+                     dim3(256), 0, stream, hist, nhist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 lgrid(lo.nblk, rows);
+  hipLaunchKernelGGL(k_long_hist<0>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_hist<1>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_hist<2>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_count, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist, cnt,
+                     thr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_write, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, cnt, thr,
+                     out, out_stride);
   return hipGetLastError();
 }
 

@@ -59,6 +59,14 @@ def test_topk_select_all_equal_and_rows_layout(rkv):
     s = np.full((3, 5000), 2.0, dtype=np.float32)
     gpu = rkv.rkv_topk_select(torch.from_numpy(s).cuda(), 777).cpu().numpy()
     assert np.array_equal(gpu, np.tile(np.arange(777), (3, 1)))
+    # rows spread over several blocks: all ties, and every element but one
+    s = np.full((2, 20000), -3.0, dtype=np.float32)
+    gpu = rkv.rkv_topk_select(torch.from_numpy(s).cuda(), 7777).cpu().numpy()
+    assert np.array_equal(gpu, np.tile(np.arange(7777), (2, 1)))
+    s = np.random.default_rng(9).standard_normal((2, 12289)).astype(np.float32)
+    gpu = rkv.rkv_topk_select(torch.from_numpy(s).cuda(), 12288).cpu().numpy()
+    for r in range(2):
+        assert np.array_equal(gpu[r], O.topk_ascending(s[r].astype(np.float64), 12288))
     s3 = np.random.default_rng(5).standard_normal((2, 3, 300)).astype(np.float32)
     g3 = rkv.rkv_topk_select(torch.from_numpy(s3).cuda(), 20).cpu().numpy()
     for b in range(2):
