@@ -32,6 +32,65 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc-k_decode_step-llama8b-L131072-bf16.json")
+COPY_CALIBRATION_BYTES = 256 << 20
+DOMINANT = "k_decode_step"
+
+
+def kernel_sources_digest() -> str:
+    """sha256 over the HIP sources and headers of the library (the counters' validity key)."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "sparse_kv_cache_snapkv_amd", "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str) -> None:
+    """Per-launch HBM traffic of the dominant kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for the plain
+    256 MiB device copy the run starts with (known bytes / counted bytes)."""
+    import csv
+
+    def dispatches(path, counter):
+        rows = []
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return sorted(rows)
+
+    out = dict(sources_sha256=kernel_sources_digest(), kernel=DOMINANT,
+               copy_bytes=COPY_CALIBRATION_BYTES)
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = dispatches(path, counter)
+        # the calibration copy is the run's first copy kernel (inputs are drawn after it)
+        copy = next(v for _, name, v in rows if "copy" in name)
+        factor = COPY_CALIBRATION_BYTES / (copy * 1024.0)
+        dom = [v for _, name, v in rows if DOMINANT in name]
+        out[counter] = dict(copy_kib=copy, factor=factor, launches=len(dom),
+                            mean_kib_per_launch=sum(dom) / len(dom),
+                            scaled_bytes_per_launch=sum(dom) / len(dom) * 1024.0 * factor)
+    out["traffic_bytes_per_launch"] = (out["FETCH_SIZE"]["scaled_bytes_per_launch"]
+                                       + out["WRITE_SIZE"]["scaled_bytes_per_launch"])
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
+def measured_traffic():
+    """Scaled HBM bytes per launch of the dominant kernel, if taken on the current sources."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            pmc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if pmc.get("sources_sha256") != kernel_sources_digest():
+        return None
+    return int(pmc["traffic_bytes_per_launch"])
 
 
 def algorithmic_bytes(w, topk: int) -> dict:
@@ -104,7 +163,14 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--cpu-sample-steps", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="start with a plain 256 MiB device copy (the counters' scale)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="write the traffic summary of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        summarize_pmc(*args.pmc_summary)
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the RocketKV path here runs on a single MI355X "
               "(no sharding or collectives are built); run with --gpus 1", file=sys.stderr)
@@ -124,6 +190,13 @@ def main() -> int:
     dcode = 1 if w.dtype == "bf16" else 0
     B, Hq, Hkv, D, Lc, P, G = w.B, w.Hq, w.Hkv, w.D, w.Lc, w.P, w.G
     scale = 1.0 / math.sqrt(D)
+
+    if args.pmc_calibration:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- inputs resident in HBM, outputs and workspaces preallocated
     prompts = [gen.device_prompt_layer(w, layer, dev) for layer in range(R)]
@@ -279,7 +352,7 @@ def main() -> int:
     roofline = dict(kernel="k_decode_step (fused decode step), mean over top-k "
                            + "/".join(str(t) for t in w.topk),
                     bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=measured_traffic(),
                     algorithmic_bytes_per_launch=int(bytes_per_launch),
                     avg_launch_us=round(dom_us, 3))
     stages = stages_out

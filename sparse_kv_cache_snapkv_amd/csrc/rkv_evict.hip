@@ -352,7 +352,8 @@ __global__ __launch_bounds__(kThreads) void k_pool(const float* __restrict__ col
   const float* src = colsum + (size_t)bh * n;
   for (int i = threadIdx.x; i < kThreads + 2 * h; i += kThreads) {
     const int j = j0 - h + i;
-    tile[i] = (j >= 0 && j < n) ? src[j] : 0.f;
+    const float x = src[min(max(j, 0), n - 1)];  // every address inside the row
+    tile[i] = (j >= 0 && j < n) ? x : 0.f;
   }
   __syncthreads();
   const int j = j0 + threadIdx.x;

@@ -313,7 +313,10 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ row, int n, i
     return E;
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = i0 + e < n ? order_key(row[i0 + e]) : 0u;
+  for (int e = 0; e < E; ++e) {
+    const float x = row[min(i0 + e, n - 1)];  // every address inside the row
+    key[e] = i0 + e < n ? order_key(x) : 0u;
+  }
   return n - i0 < 0 ? 0 : (n - i0 > E ? E : n - i0);
 }
 

@@ -93,7 +93,9 @@ __device__ __forceinline__ void find_digit(const uint32_t* __restrict__ hist, in
   uint32_t c[8], local = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    c[j] = j < bpt ? hist[nbins - 1 - (tid * bpt + j)] : 0u;
+    const int bin = nbins - 1 - (tid * bpt + j);  // negative only when j >= bpt
+    const uint32_t x = hist[bin < 0 ? 0 : bin];
+    c[j] = j < bpt ? x : 0u;
     local += c[j];
   }
   uint32_t excl, unused, tot, unused2;
