@@ -76,6 +76,25 @@ EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int keep, int dtype
 
 // ---------------------------------------------------------------------------- MFMA (bf16) passes
 
+// K rows of one wave's 64 keys (two 32-key tiles), in the permuted head-dim order of the MFMA
+// operands: lane (half hf, row n) holds channels hf*D/2 + 8s .. +8 of key key0 + kt*32 + n.
+template <int D>
+__device__ __forceinline__ void load_key_tiles(const bf16_t* __restrict__ k_bh, int key0,
+                                               int last, int hf, int n,
+                                               bf16x8 (&kf)[2][D / 16]) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = min(key0 + kt * 32 + n, last);
+    const bf16_t* kr = k_bh + (size_t)key * D + hf * (D / 2);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) kf[kt][s] = *reinterpret_cast<const bf16x8*>(kr + s * 8);
+  }
+}
+
+// Pass 1: per window row, the running (max, sum of exp2) of its scaled logits over this block's
+// keys, in log2 units. Each lane keeps the running pair of its row in every 32-row tile across
+// all of the block's key groups; the pairs of the lane halves and the four waves merge once at
+// the end.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __restrict__ q_win,
                                                              const bf16_t* __restrict__ k, int L,
@@ -84,12 +103,12 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
                                                              float2* __restrict__ stats) {
   constexpr int KS = D / 16;
   constexpr int QS = D + 8;
+  constexpr int kMaxTiles = 16;  // GW <= 512
   extern __shared__ __align__(16) uint16_t smem[];
   const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y, chunk = blockIdx.x;
-  float2* run = reinterpret_cast<float2*>(smem + (size_t)GWp * QS);
-  float2* wst = run + GWp;
+  float2* wst = reinterpret_cast<float2*>(smem + (size_t)GWp * QS);  // [4][GWp]
 
   const bf16_t* qg = q_win + (size_t)bh * GW * D;
   for (int idx = tid; idx < GWp * (D / 8); idx += kThreads) {
@@ -98,20 +117,25 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
     if (row < GW) val = load16(qg + (size_t)row * D + c8 * 8);
     *reinterpret_cast<uint4*>(smem + (size_t)row * QS + c8 * 8) = val;
   }
-  for (int r = tid; r < GWp; r += kThreads) run[r] = make_float2(-INFINITY, 0.f);
   __syncthreads();
 
+  float m[kMaxTiles], l[kMaxTiles];
+#pragma unroll
+  for (int rt = 0; rt < kMaxTiles; ++rt) {
+    m[rt] = -INFINITY;
+    l[rt] = 0.f;
+  }
+  const bf16_t* k_bh = k + (size_t)bh * L * D;
+  const int first = chunk * nsub * kKeysPerSub + wave * 64;
+  bf16x8 kf[2][KS];
+  load_key_tiles<D>(k_bh, first, L - 1, hf, n, kf);
   for (int sub = 0; sub < nsub; ++sub) {
-    const int key0 = (chunk * nsub + sub) * kKeysPerSub + wave * 64;
-    bf16x8 kf[2][KS];
+    const int key0 = first + sub * kKeysPerSub;
+    // keys below L-W are visible to every window row: only groups reaching it need the mask
+    const bool masked = key0 + 63 >= L - W;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = min(key0 + kt * 32 + n, L - 1);
-      const bf16_t* kr = k + ((size_t)bh * L + key) * D + hf * (D / 2);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[kt][s] = *reinterpret_cast<const bf16x8*>(kr + s * 8);
-    }
-    for (int rt = 0; rt < NRT; ++rt) {
+    for (int rt = 0; rt < kMaxTiles; ++rt) {
+      if (rt >= NRT) break;
       f32x16 acc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -125,49 +149,63 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
         acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][s], qf, acc[1], 0, 0, 0);
       }
       // lane holds window row rt*32+n against keys key0 + kt*32 + 8*(i/4) + 4*hf + i%4
-      const int row = rt * 32 + n;
-      const int lim = row < GW ? L - W + (row % W) : -1;  // last visible key
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const float v = (key < L && key <= lim) ? acc[kt][i] * scale2 : -INFINITY;
-          acc[kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float sm = 0.f;
-      if (mx != -INFINITY) {
+      if (masked) {
+        const int row = rt * 32 + n;
+        const int lim = row < GW ? L - W + (row % W) : -1;  // last visible key
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sm += exp2f(acc[kt][i] - mx);
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + kt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+            acc[kt][i] = (key < L && key <= lim) ? acc[kt][i] : -INFINITY;
+          }
       }
-      sm += __shfl_xor(sm, 32, 64);
-      if (hf == 0) wst[wave * GWp + row] = make_float2(mx, sm);
-    }
-    __syncthreads();
-    for (int r = tid; r < GWp; r += kThreads) {
-      float m = run[r].x, l = run[r].y;
+      float tmax = acc[0][0];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float2 x = wst[w * GWp + r];
-        const float M = fmaxf(m, x.x);
-        if (M != -INFINITY) {
-          l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
-          m = M;
-        }
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[kt][i]);
+      const float mn = fmaxf(m[rt], tmax * scale2);  // scale2 > 0: the scaled max
+      if (mn != -INFINITY) {
+        float sm = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sm += exp2f(fmaf(acc[kt][i], scale2, -mn));
+        l[rt] = l[rt] * exp2f(m[rt] - mn) + sm;
+        m[rt] = mn;
       }
-      run[r] = make_float2(m, l);
     }
-    __syncthreads();
+    if (sub + 1 < nsub) load_key_tiles<D>(k_bh, key0 + kKeysPerSub, L - 1, hf, n, kf);
   }
-  for (int r = tid; r < GW; r += kThreads)
-    stats[((size_t)bh * nchunk + chunk) * GWp + r] = run[r];
+  // merge the two lane halves (same rows, other keys), then the waves through LDS
+#pragma unroll
+  for (int rt = 0; rt < kMaxTiles; ++rt) {
+    if (rt >= NRT) break;
+    const float mo = __shfl_xor(m[rt], 32, 64), lo = __shfl_xor(l[rt], 32, 64);
+    const float mx = fmaxf(m[rt], mo);
+    const float lx = mx == -INFINITY ? 0.f : l[rt] * exp2f(m[rt] - mx) + lo * exp2f(mo - mx);
+    if (hf == 0) wst[wave * GWp + rt * 32 + n] = make_float2(mx, lx);
+  }
+  __syncthreads();
+  for (int r = tid; r < GW; r += kThreads) {
+    float mm = -INFINITY, ll = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float2 x = wst[w * GWp + r];
+      const float M = fmaxf(mm, x.x);
+      if (M != -INFINITY) {
+        ll = ll * exp2f(mm - M) + x.y * exp2f(x.x - M);
+        mm = M;
+      }
+    }
+    stats[((size_t)bh * nchunk + chunk) * GWp + r] = make_float2(mm, ll);
+  }
 }
 
+// Pass 2: for each prefix key, the sum over the group's window rows of exp2(scaled logit - row
+// log-sum-exp), i.e. its softmax probabilities summed over the G*W rows. Prefix keys are visible
+// to every row, so no mask is needed.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __restrict__ q_win,
                                                               const bf16_t* __restrict__ k,
@@ -180,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
   extern __shared__ __align__(16) uint16_t smem[];
   const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
+  // blocks walk the keys in the reverse of pass 1's order: the K rows pass 1 read last are the
+  // ones still held by the Infinity Cache when this pass starts
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int nprefix = L - W;
   float* s_lse = reinterpret_cast<float*>(smem + (size_t)GWp * QS);
@@ -191,21 +231,21 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
     if (row < GW) val = load16(qg + (size_t)row * D + c8 * 8);
     *reinterpret_cast<uint4*>(smem + (size_t)row * QS + c8 * 8) = val;
   }
-  for (int r = tid; r < GWp; r += kThreads)
-    s_lse[r] = r < GW ? lse[(size_t)bh * GWp + r] : INFINITY;  // padded rows add exp2(-inf) = 0
+  for (int r = tid; r < GWp; r += kThreads) {
+    const float x = lse[(size_t)bh * GWp + min(r, GW - 1)];
+    s_lse[r] = r < GW ? x : INFINITY;  // padded rows add exp2(-inf) = 0
+  }
   __syncthreads();
 
+  const bf16_t* k_bh = k + (size_t)bh * L * D;
+  const int first = chunk * nsub * kKeysPerSub + wave * 64;
+  if (first >= nprefix) return;  // no barrier below: waves may leave independently
+  bf16x8 kf[2][KS];
+  load_key_tiles<D>(k_bh, first, nprefix - 1, hf, n, kf);
   for (int sub = 0; sub < nsub; ++sub) {
-    const int key0 = (chunk * nsub + sub) * kKeysPerSub + wave * 64;
-    if (key0 >= nprefix) break;  // no barrier below: waves may leave independently
-    bf16x8 kf[2][KS];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = min(key0 + kt * 32 + n, nprefix - 1);
-      const bf16_t* kr = k + ((size_t)bh * L + key) * D + hf * (D / 2);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[kt][s] = *reinterpret_cast<const bf16x8*>(kr + s * 8);
-    }
+    const int key0 = first + sub * kKeysPerSub;
+    if (key0 >= nprefix) break;
+    const bool more = sub + 1 < nsub && key0 + kKeysPerSub < nprefix;
     float cs[2] = {0.f, 0.f};
     for (int rt = 0; rt < NRT; ++rt) {
       f32x16 acc[2];
@@ -224,8 +264,8 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float ls = s_lse[rt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)];
-        cs[0] += exp2f(acc[0][i] * scale2 - ls);
-        cs[1] += exp2f(acc[1][i] * scale2 - ls);
+        cs[0] += exp2f(fmaf(acc[0][i], scale2, -ls));
+        cs[1] += exp2f(fmaf(acc[1][i], scale2, -ls));
       }
     }
 #pragma unroll
@@ -234,6 +274,7 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
       const int key = key0 + kt * 32 + n;
       if (hf == 0 && key < nprefix) colsum[(size_t)bh * nprefix + key] = tot;
     }
+    if (more) load_key_tiles<D>(k_bh, key0 + kKeysPerSub, nprefix - 1, hf, n, kf);
   }
 }
 
@@ -323,28 +364,35 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_f32(const float* __rest
 
 // ---------------------------------------------------------------------------- shared stages
 
+// Per window row, the log2-sum-exp of its scaled logits from the pass-1 chunk pairs: one wave per
+// row, lanes over chunks (online merge per lane), then a wave-wide merge.
 __global__ __launch_bounds__(kThreads) void k_win_lse(const float2* __restrict__ stats, int nchunk,
                                                       int GW, float* __restrict__ lse) {
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   const int GWp = (GW + 31) & ~31;
-  for (int r = threadIdx.x; r < GW; r += kThreads) {
-    float m = -INFINITY, l = 0.f;
-    for (int c = 0; c < nchunk; ++c) {
-      const float2 x = stats[((size_t)bh * nchunk + c) * GWp + r];
-      const float M = fmaxf(m, x.x);
-      if (M != -INFINITY) {
-        l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
-        m = M;
-      }
+  if (r >= GW) return;  // whole waves leave together; no barrier follows
+  float m = -INFINITY, l = 0.f;
+  for (int c = lane; c < nchunk; c += kWave) {
+    const float2 x = stats[((size_t)bh * nchunk + c) * GWp + r];
+    const float M = fmaxf(m, x.x);
+    if (M != -INFINITY) {
+      l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
+      m = M;
     }
-    lse[(size_t)bh * GWp + r] = m + log2f(l);
   }
+  const float M = group_max<kWave>(m);
+  const float part = M == -INFINITY ? 0.f : l * exp2f(m - M);
+  const float tot = group_sum<kWave>(part);
+  if (lane == 0) lse[(size_t)bh * GWp + r] = M + log2f(tot);
 }
 
-// Zero-padded same-size pooling of each row; the tile and its halo are staged in LDS.
+// Zero-padded same-size pooling of each row (KIND 0: box average, 1: box maximum); the tile and
+// its halo are staged in LDS.
+template <int KIND>
 __global__ __launch_bounds__(kThreads) void k_pool(const float* __restrict__ colsum, int n,
-                                                   int kernel, int kind,
-                                                   float* __restrict__ pooled) {
+                                                   int kernel, float* __restrict__ pooled) {
   __shared__ float tile[kThreads + 128];
   const int bh = blockIdx.y;
   const int h = kernel / 2;
@@ -358,12 +406,20 @@ __global__ __launch_bounds__(kThreads) void k_pool(const float* __restrict__ col
   __syncthreads();
   const int j = j0 + threadIdx.x;
   if (j >= n) return;
-  float acc = kind == 0 ? 0.f : tile[threadIdx.x];
-  for (int u = 0; u < kernel; ++u) {
-    const float x = tile[threadIdx.x + u];
-    acc = kind == 0 ? acc + x : fmaxf(acc, x);
+  // four interleaved partial results keep the dependent chains short
+  const float* t = tile + threadIdx.x;
+  float a[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] = KIND == 0 ? 0.f : t[0];
+  int u = 0;
+  for (; u + 4 <= kernel; u += 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = KIND == 0 ? a[e] + t[u + e] : fmaxf(a[e], t[u + e]);
   }
-  pooled[(size_t)bh * n + j] = kind == 0 ? acc / (float)kernel : acc;
+  for (; u < kernel; ++u) a[0] = KIND == 0 ? a[0] + t[u] : fmaxf(a[0], t[u]);
+  const float acc = KIND == 0 ? (a[0] + a[1]) + (a[2] + a[3])
+                              : fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+  pooled[(size_t)bh * n + j] = KIND == 0 ? acc / (float)kernel : acc;
 }
 
 // Completes kept_idx (window positions, or the identity when nothing is evicted) and gathers
@@ -437,7 +493,8 @@ hipError_t scores_bf16(const void* q_win, const void* k, int BH, int L, int W,
                      lo.GW, lo.nsub1, lo.nchunk1, scale2, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_win_lse, dim3(BH), dim3(kThreads), 0, stream, stats, lo.nchunk1, lo.GW, lse);
+  hipLaunchKernelGGL(k_win_lse, dim3((lo.GW + 3) / 4, BH), dim3(kThreads), 0, stream, stats,
+                     lo.nchunk1, lo.GW, lse);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_win_colsum_mfma<D>, dim3(lo.nchunk2, BH), dim3(kThreads), lds2, stream,
                      static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), lse, L, W,
@@ -457,7 +514,8 @@ hipError_t scores_f32(const void* q_win, const void* k, int BH, int L, int W,
                      static_cast<const float*>(k), L, W, lo.GW, nchunk, scale2, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_win_lse, dim3(BH), dim3(kThreads), 0, stream, stats, nchunk, lo.GW, lse);
+  hipLaunchKernelGGL(k_win_lse, dim3((lo.GW + 3) / 4, BH), dim3(kThreads), 0, stream, stats,
+                     nchunk, lo.GW, lse);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_win_colsum_f32<D>, dim3((lo.nprefix + kThreads - 1) / kThreads, BH),
                      dim3(kThreads), 0, stream, static_cast<const float*>(q_win),
@@ -494,8 +552,12 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
   const int n = lo.nprefix;
   float* colsum = reinterpret_cast<float*>(w + lo.off_colsum);
   float* pooled = pooled_out != nullptr ? pooled_out : reinterpret_cast<float*>(w + lo.off_pooled);
-  hipLaunchKernelGGL(k_pool, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, stream,
-                     colsum, n, pool_kernel, pool_type, pooled);
+  if (pool_type == 0)
+    hipLaunchKernelGGL(k_pool<0>, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0,
+                       stream, colsum, n, pool_kernel, pooled);
+  else
+    hipLaunchKernelGGL(k_pool<1>, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0,
+                       stream, colsum, n, pool_kernel, pooled);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_topk(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk, stream)) !=
       hipSuccess)
