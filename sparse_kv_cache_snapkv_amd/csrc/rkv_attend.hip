@@ -127,7 +127,7 @@ struct WaveState {
         for (int s = 1; s < kSlots; ++s) x = fmaxf(x, sc[s][g]);
         x = across_max<LPT>(x);
         const float mn = fmaxf(m[g], x);
-        const float f = mn == -INFINITY ? 1.f : exp2f(m[g] - mn);
+        const float f = mn == -INFINITY ? 1.f : exp2_hw(m[g] - mn);
         mu[g] = mn == -INFINITY ? 0.f : mn;
         m[g] = mn;
         l[g] *= f;
@@ -140,7 +140,7 @@ struct WaveState {
         unpack16<T>(vr[s], vf);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float p = exp2f(sc[s][g] - mu[g]);
+          const float p = exp2_hw(sc[s][g] - mu[g]);
           l[g] += p;
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
@@ -186,7 +186,7 @@ __device__ __forceinline__ void wave_merge(const AttendShared<D, G>& sh, int g, 
   if (M == -INFINITY) return;
 #pragma unroll
   for (int w = 0; w < kWavesPerBlock; ++w) {
-    const float fw = exp2f(sh.m[w][g] - M);
+    const float fw = exp2_hw(sh.m[w][g] - M);
     lsum = fmaf(sh.l[w][g], fw, lsum);
     o = fmaf(sh.o[w][g][c], fw, o);
   }
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_merge(const float* __restri
     float lsum = 0.f;
     for (int s = lane; s < nsplit; s += kWave) {
       const float ms = hp[s * stride + g * (D + 2) + D];
-      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      const float w = ms == -INFINITY ? 0.f : exp2_hw(ms - M);
       s_w[s][g] = w;
       lsum = fmaf(hp[s * stride + g * (D + 2) + D + 1], w, lsum);
     }
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     for (int gg = wave; gg < ng; gg += kWavesPerBlock) {  // lane = split
       const float ms = lane < nsa ? mg.m[lane][gg] : -INFINITY;
       const float M = group_max<kWave>(ms);
-      const float wgt = (lane < nsa && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
+      const float wgt = (lane < nsa && ms != -INFINITY) ? exp2_hw(ms - M) : 0.f;
       const float lsum = group_sum<kWave>(lane < nsa ? mg.l[lane][gg] * wgt : 0.f);
       if (lane < nsa) mg.m[lane][gg] = wgt;
       if (lane == 0) mg.inv[gg] = lsum > 0.f ? 1.f / lsum : 0.f;

@@ -230,4 +230,10 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 2^x by the hardware instruction alone (v_exp_f32): results below the smallest normal float
+// come out as zero, which the softmax sums and rescaling factors here tolerate, and 2^-inf = 0.
+// The library exp2f wraps the same instruction in a rescaling for such results, several times
+// the instructions on every element.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 }  // namespace rkv

@@ -171,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sm += exp2f(fmaf(acc[kt][i], scale2, -mn));
-        l[rt] = l[rt] * exp2f(m[rt] - mn) + sm;
+          for (int i = 0; i < 16; ++i) sm += exp2_hw(fmaf(acc[kt][i], scale2, -mn));
+        l[rt] = l[rt] * exp2_hw(m[rt] - mn) + sm;
         m[rt] = mn;
       }
     }
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
     if (rt >= NRT) break;
     const float mo = __shfl_xor(m[rt], 32, 64), lo = __shfl_xor(l[rt], 32, 64);
     const float mx = fmaxf(m[rt], mo);
-    const float lx = mx == -INFINITY ? 0.f : l[rt] * exp2f(m[rt] - mx) + lo * exp2f(mo - mx);
+    const float lx = mx == -INFINITY ? 0.f : l[rt] * exp2_hw(m[rt] - mx) + lo * exp2_hw(mo - mx);
     if (hf == 0) wst[wave * GWp + rt * 32 + n] = make_float2(mx, lx);
   }
   __syncthreads();
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
       const float2 x = wst[w * GWp + r];
       const float M = fmaxf(mm, x.x);
       if (M != -INFINITY) {
-        ll = ll * exp2f(mm - M) + x.y * exp2f(x.x - M);
+        ll = ll * exp2_hw(mm - M) + x.y * exp2_hw(x.x - M);
         mm = M;
       }
     }
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float ls = s_lse[rt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)];
-        cs[0] += exp2f(fmaf(acc[0][i], scale2, -ls));
-        cs[1] += exp2f(fmaf(acc[1][i], scale2, -ls));
+        cs[0] += exp2_hw(fmaf(acc[0][i], scale2, -ls));
+        cs[1] += exp2_hw(fmaf(acc[1][i], scale2, -ls));
       }
     }
 #pragma unroll
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_f32(const float* __restr
     const bool valid = key < L && key <= L - W + (row % W);
     const float v = valid ? d * scale2 : -INFINITY;
     const float m = group_max<64>(v);
-    float sm = m != -INFINITY ? exp2f(v - m) : 0.f;
+    float sm = m != -INFINITY ? exp2_hw(v - m) : 0.f;
     sm = group_sum<64>(sm);
     if (lane == 0) wst[wave * GW + row] = make_float2(m, sm);
   }
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_f32(const float* __restr
       const float2 x = wst[w * GW + r];
       const float M = fmaxf(m, x.x);
       if (M != -INFINITY) {
-        l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
+        l = l * exp2_hw(m - M) + x.y * exp2_hw(x.x - M);
         m = M;
       }
     }
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_f32(const float* __rest
     float d = 0.f;
 #pragma unroll
     for (int c = 0; c < D; ++c) d = fmaf(qr[c], kv[c], d);
-    cs += exp2f(d * scale2 - lb[row]);
+    cs += exp2_hw(d * scale2 - lb[row]);
   }
   colsum[(size_t)bh * nprefix + key] = cs;
 }
@@ -378,12 +378,12 @@ __global__ __launch_bounds__(kThreads) void k_win_lse(const float2* __restrict__
     const float2 x = stats[((size_t)bh * nchunk + c) * GWp + r];
     const float M = fmaxf(m, x.x);
     if (M != -INFINITY) {
-      l = l * exp2f(m - M) + x.y * exp2f(x.x - M);
+      l = l * exp2_hw(m - M) + x.y * exp2_hw(x.x - M);
       m = M;
     }
   }
   const float M = group_max<kWave>(m);
-  const float part = M == -INFINITY ? 0.f : l * exp2f(m - M);
+  const float part = M == -INFINITY ? 0.f : l * exp2_hw(m - M);
   const float tot = group_sum<kWave>(part);
   if (lane == 0) lse[(size_t)bh * GWp + r] = M + log2f(tot);
 }
