@@ -329,16 +329,17 @@ __device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float(
 // turned current, so the waiting readers of a whole grid add little traffic. Bounded: on give-up
 // the status word is set and the stale values are used. Call with the whole wave (the exit is
 // wave-uniform).
-template <int N, typename Addr>
-__device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[N], Addr&& addr,
-                                            unsigned epoch, unsigned* status) {
+template <int N>
+__device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[N],
+                                            const uint64_t* const (&ptr)[N], unsigned epoch,
+                                            unsigned* status) {
 #pragma unroll
-  for (int j = 0; j < N; ++j) w[j] = use[j] ? ld_coherent(addr(j)) : 0ull;
+  for (int j = 0; j < N; ++j) w[j] = use[j] ? ld_coherent(ptr[j]) : 0ull;
   for (int polls = 0;; ++polls) {
     const uint64_t* first_stale = nullptr;
 #pragma unroll
     for (int j = N - 1; j >= 0; --j)
-      if (use[j] && !tag_is(w[j], epoch)) first_stale = addr(j);
+      if (use[j] && !tag_is(w[j], epoch)) first_stale = ptr[j];
     const uint64_t waiting = __ballot(first_stale != nullptr);
     if (waiting == 0ull) return;
     if (polls > kSpinLimit) {
@@ -355,7 +356,7 @@ __device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[
     if (tag_is(ld_coherent(probe), epoch)) {
 #pragma unroll
       for (int j = 0; j < N; ++j)
-        if (use[j] && !tag_is(w[j], epoch)) w[j] = ld_coherent(addr(j));
+        if (use[j] && !tag_is(w[j], epoch)) w[j] = ld_coherent(ptr[j]);
     }
   }
 }
@@ -385,7 +386,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   float* s_scores = u.scores;
   __shared__ SelectShared<kThreads> sel;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int bh = blockIdx.y, split = blockIdx.x, b = bh / a.Hkv, h = bh % a.Hkv;
+  // grid (BH, nsplit): consecutive blocks belong to different heads, so the round-robin
+  // placement of blocks on the XCDs keeps every block of a head on one XCD when BH is a
+  // multiple of 8 (its summaries rows and exchanged words then stay in that XCD's L2)
+  const int bh = blockIdx.x, split = blockIdx.y, b = bh / a.Hkv, h = bh % a.Hkv;
   const T* q = static_cast<const T*>(a.q);
   const bool multi = a.nsplit > 1;
   const bool attends = split < a.nsplit_att;
@@ -431,7 +435,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     bool use[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) use[j] = j * kThreads + tid < a.P;
-    load_tagged<E>(w, use, [&](int j) { return xs + j * kThreads + tid; }, epoch, a.sync);
+    const uint64_t* ptr[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) ptr[j] = xs + min(j * kThreads + tid, a.P - 1);
+    load_tagged<E>(w, use, ptr, epoch, a.sync);
 #pragma unroll
     for (int j = 0; j < E; ++j)
       if (use[j]) s_scores[j * kThreads + tid] = tag_value(w[j]);
@@ -512,31 +519,50 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     const int ne = min(cpb, G * D - e0);
     if (ne <= 0) return;  // (never split 0)
     const int g0 = e0 / D, ng = (e0 + ne - 1) / D - g0 + 1;
-    const int n_o = nsa * ne, n_all = n_o + 2 * nsa * ng;
     MergeShared<D, G>& mg = u.mg;
     __syncthreads();  // the attention scratch is dead from here on
+    // Items, indexed without division: o of (split s, element e) at s * NEP + e for e < ne (NEP
+    // = ne rounded up to a power of two), then (max, sum) of (split s, group gg) at
+    // NO + (which * kMaxSplit + s) * 8 + gg for gg < ng.
+    const int lne = 32 - __clz(ne - 1);  // log2 of NEP
+    const int NO = nsa << lne;
+    const int n_all = NO + 2 * kMaxSplit * 8;
     for (int base = 0; base < n_all; base += kMergePer * kThreads) {
       uint64_t w[kMergePer];
       bool use[kMergePer];
-#pragma unroll
-      for (int j = 0; j < kMergePer; ++j) use[j] = base + j * kThreads + tid < n_all;
-      auto addr = [&](int j) -> const uint64_t* {
-        const int i = base + j * kThreads + tid;
-        if (i < n_o) return hp + (size_t)(i / ne) * kStride + e0 + i % ne;
-        const int t = i - n_o, which = t / (nsa * ng), rem = t % (nsa * ng);
-        return hp + (size_t)(rem / ng) * kStride + G * D + which * G + g0 + rem % ng;
-      };
-      load_tagged<kMergePer>(w, use, addr, epoch, a.sync);
+      const uint64_t* ptr[kMergePer];
+      int dst[kMergePer];  // LDS slot: o index, or -1 - (which * kMaxSplit * G + s * G + gg)
 #pragma unroll
       for (int j = 0; j < kMergePer; ++j) {
         const int i = base + j * kThreads + tid;
+        bool u_ = false;
+        const uint64_t* pp = hp;
+        int d = 0;
+        if (i < NO) {
+          const int sp = i >> lne, e = i & ((1 << lne) - 1);
+          u_ = e < ne;
+          pp = hp + (size_t)sp * kStride + e0 + min(e, ne - 1);
+          d = sp * ne + e;
+        } else if (i < n_all) {
+          const int t = i - NO, gg = t & 7, sp = (t >> 3) & (kMaxSplit - 1), which = t >> 9;
+          u_ = sp < nsa && gg < ng;
+          pp = hp + (size_t)min(sp, nsa - 1) * kStride + G * D + which * G + g0 + min(gg, ng - 1);
+          d = -1 - ((which * kMaxSplit + sp) * G + gg);
+        }
+        use[j] = u_;
+        ptr[j] = pp;
+        dst[j] = d;
+      }
+      load_tagged<kMergePer>(w, use, ptr, epoch, a.sync);
+#pragma unroll
+      for (int j = 0; j < kMergePer; ++j) {
         if (!use[j]) continue;
         const float v = tag_value(w[j]);
-        if (i < n_o) {
-          mg.o[i] = v;
+        if (dst[j] >= 0) {
+          mg.o[dst[j]] = v;
         } else {
-          const int t = i - n_o, which = t / (nsa * ng), rem = t % (nsa * ng);
-          (which == 0 ? mg.m : mg.l)[rem / ng][rem % ng] = v;
+          const int d = -1 - dst[j], which = d / (kMaxSplit * G), r = d % (kMaxSplit * G);
+          (which == 0 ? mg.m : mg.l)[r / G][r % G] = v;
         }
       }
     }
@@ -634,10 +660,10 @@ hipError_t attend_g(AttendArgs a, int BH, hipStream_t stream) {
 template <typename T, int D, int G>
 hipError_t step_g(StepArgs a, int BH, hipStream_t stream) {
   if (a.P <= 16 * kThreads)
-    hipLaunchKernelGGL((k_decode_step<T, D, G, 16>), dim3(a.nsplit, BH), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_decode_step<T, D, G, 16>), dim3(BH, a.nsplit), dim3(kThreads), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((k_decode_step<T, D, G, 32>), dim3(a.nsplit, BH), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_decode_step<T, D, G, 32>), dim3(BH, a.nsplit), dim3(kThreads), 0,
                        stream, a);
   return hipGetLastError();
 }
