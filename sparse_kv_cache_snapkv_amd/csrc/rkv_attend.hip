@@ -36,34 +36,35 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kSlots = 4;            // row loads per wave per chunk
+constexpr int kSlots = 4;            // row loads per wave per chunk (standalone attention)
 constexpr int kMaxPagesPerSplit = 1024;
 
 constexpr int kSpinLimit = 1 << 20;  // polls before a head's cross-block wait gives up
 
-template <typename T, int D>
+template <typename T, int D, int SLOTS = kSlots>
 struct Geo {
   static constexpr int V = vec16<T>::n;
   static constexpr int LPT = D / V;
   static constexpr int TPL = kWave / LPT;
-  static constexpr int WTOK = kSlots * TPL;  // tokens per wave per chunk
+  static constexpr int WTOK = SLOTS * TPL;  // tokens per wave per chunk
 };
 
-template <int D, int G>
+template <int D, int G, int NW = kWavesPerBlock>
 struct AttendShared {
   int pages[kMaxPagesPerSplit + kWave];  // slots from kMaxPagesPerSplit: discarded writes, per lane
-  float m[kWavesPerBlock][G], l[kWavesPerBlock][G];
-  float o[kWavesPerBlock][G][D];
+  float m[NW][G], l[NW][G];
+  float o[NW][G][D];
 };
 
-// Per-wave online-softmax state of the G heads of a group.
-template <typename T, int D, int G>
+// Per-wave online-softmax state of the G heads of a group; NW waves share a block's page list and
+// each issues SLOTS K and V row loads per chunk.
+template <typename T, int D, int G, int NW = kWavesPerBlock, int SLOTS = kSlots>
 struct WaveState {
-  float qf[G][Geo<T, D>::V];
-  float m[G], l[G], acc[G][Geo<T, D>::V];
+  float qf[G][Geo<T, D, SLOTS>::V];
+  float m[G], l[G], acc[G][Geo<T, D, SLOTS>::V];
 
   __device__ __forceinline__ void init(const T* __restrict__ q_bh, float scale2) {
-    constexpr int V = Geo<T, D>::V, LPT = Geo<T, D>::LPT;
+    constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT;
     const int li = (threadIdx.x & (kWave - 1)) % LPT;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -80,17 +81,17 @@ struct WaveState {
   // Tokens [0, ntok) of the page list `pages` (LDS): this wave takes chunks wave, wave+4, ...
   __device__ __forceinline__ void run(const T* __restrict__ kc_bh, const T* __restrict__ vc_bh,
                                       const int* pages, int ntok, int ps, int P, int Lc) {
-    constexpr int V = Geo<T, D>::V, LPT = Geo<T, D>::LPT, TPL = Geo<T, D>::TPL;
-    constexpr int WTOK = Geo<T, D>::WTOK;
+    constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT, TPL = Geo<T, D, SLOTS>::TPL;
+    constexpr int WTOK = Geo<T, D, SLOTS>::WTOK;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int lg = lane / LPT, li = lane % LPT;
     const T* kb = kc_bh + li * V;
     const T* vb = vc_bh + li * V;
-    for (int c0 = wave * WTOK; c0 < ntok; c0 += kWavesPerBlock * WTOK) {
-      int tok[kSlots];
-      bool ok[kSlots];
+    for (int c0 = wave * WTOK; c0 < ntok; c0 += NW * WTOK) {
+      int tok[SLOTS];
+      bool ok[SLOTS];
 #pragma unroll
-      for (int s = 0; s < kSlots; ++s) {
+      for (int s = 0; s < SLOTS; ++s) {
         const int ti = c0 + s * TPL + lg;
         bool valid = ti < ntok;
         const int page = valid ? pages[ti / ps] : 0;
@@ -99,15 +100,15 @@ struct WaveState {
         ok[s] = valid;
         tok[s] = valid ? t : 0;
       }
-      uint4 kr[kSlots], vr[kSlots];
+      uint4 kr[SLOTS], vr[SLOTS];
 #pragma unroll
-      for (int s = 0; s < kSlots; ++s) {
+      for (int s = 0; s < SLOTS; ++s) {
         kr[s] = load16_stream(kb + (size_t)tok[s] * D);
         vr[s] = load16_stream(vb + (size_t)tok[s] * D);
       }
-      float sc[kSlots][G];
+      float sc[SLOTS][G];
 #pragma unroll
-      for (int s = 0; s < kSlots; ++s) {
+      for (int s = 0; s < SLOTS; ++s) {
         float kf[V];
         unpack16<T>(kr[s], kf);
 #pragma unroll
@@ -124,7 +125,7 @@ struct WaveState {
       for (int g = 0; g < G; ++g) {
         float x = sc[0][g];
 #pragma unroll
-        for (int s = 1; s < kSlots; ++s) x = fmaxf(x, sc[s][g]);
+        for (int s = 1; s < SLOTS; ++s) x = fmaxf(x, sc[s][g]);
         x = across_max<LPT>(x);
         const float mn = fmaxf(m[g], x);
         const float f = mn == -INFINITY ? 1.f : exp2_hw(m[g] - mn);
@@ -135,7 +136,7 @@ struct WaveState {
         for (int e = 0; e < V; ++e) acc[g][e] *= f;
       }
 #pragma unroll
-      for (int s = 0; s < kSlots; ++s) {
+      for (int s = 0; s < SLOTS; ++s) {
         float vf[V];
         unpack16<T>(vr[s], vf);
 #pragma unroll
@@ -150,8 +151,8 @@ struct WaveState {
   }
 
   // Reduces over the wave's lane groups and stores (m, l, o) of this wave in sh.
-  __device__ __forceinline__ void publish(AttendShared<D, G>& sh) {
-    constexpr int V = Geo<T, D>::V, LPT = Geo<T, D>::LPT;
+  __device__ __forceinline__ void publish(AttendShared<D, G, NW>& sh) {
+    constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int lg = lane / LPT, li = lane % LPT;
 #pragma unroll
@@ -174,18 +175,18 @@ struct WaveState {
   }
 };
 
-// Combines the four waves' (m, l, o) for output element idx = g*D + c.
-template <int D, int G>
-__device__ __forceinline__ void wave_merge(const AttendShared<D, G>& sh, int g, int c, float& M,
+// Combines the NW waves' (m, l, o) for output element idx = g*D + c.
+template <int D, int G, int NW = kWavesPerBlock>
+__device__ __forceinline__ void wave_merge(const AttendShared<D, G, NW>& sh, int g, int c, float& M,
                                            float& lsum, float& o) {
   M = sh.m[0][g];
 #pragma unroll
-  for (int w = 1; w < kWavesPerBlock; ++w) M = fmaxf(M, sh.m[w][g]);
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sh.m[w][g]);
   lsum = 0.f;
   o = 0.f;
   if (M == -INFINITY) return;
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float fw = exp2_hw(sh.m[w][g] - M);
     lsum = fmaf(sh.l[w][g], fw, lsum);
     o = fmaf(sh.o[w][g][c], fw, o);
@@ -282,6 +283,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_merge(const float* __restri
 // ------------------------------------------------------------------------------ fused step
 
 constexpr int kMaxSplit = 64;  // blocks per head in the fused step
+constexpr int kStepThreads = 512;  // threads of a fused-step block: two waves per SIMD
+constexpr int kStepWaves = kStepThreads / kWave;
+constexpr int kStepSlots = 4;       // row loads per wave per chunk in the fused step
+constexpr int kStepSoloTokens = 128;  // budgets up to this many tokens: one attending block
 
 // Cross-block data of the fused step is exchanged as 64-bit words {value bits, epoch}: every
 // block of a head reads the head's epoch word at the start, tags what it publishes with
@@ -372,19 +377,19 @@ struct MergeShared {
 constexpr int kMergePer = 8;  // tagged words a thread loads per round of the merge
 
 template <typename T, int D, int G, int E>
-__global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
+__global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
   __shared__ ChannelShared ch;
   // The head's scores are dead once the keys are in registers (block_threshold passes a barrier
   // before any page-list or attention write), so they share LDS with the attention scratch; the
   // merge scratch comes after the attention's last read of it.
   __shared__ union {
-    __align__(16) float scores[E * kThreads];
-    AttendShared<D, G> att;
+    __align__(16) float scores[E * kStepThreads];
+    AttendShared<D, G, kStepWaves> att;
     MergeShared<D, G> mg;
   } u;
-  AttendShared<D, G>& sh = u.att;
+  AttendShared<D, G, kStepWaves>& sh = u.att;
   float* s_scores = u.scores;
-  __shared__ SelectShared<kThreads> sel;
+  __shared__ SelectShared<kStepThreads> sel;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   // grid (BH, nsplit): consecutive blocks belong to different heads, so the round-robin
   // placement of blocks on the XCDs keeps every block of a head on one XCD when BH is a
@@ -400,13 +405,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     if (epoch == 0u) epoch = 1u;  // tag 0 is what a cleared workspace holds
   }
 
-  WaveState<T, D, G> st;  // the queries' loads overlap the channel selection
+  WaveState<T, D, G, kStepWaves, kStepSlots> st;  // the queries' loads overlap the channel selection
   if (attends) st.init(q + (size_t)bh * G * D, a.scale2);
 
   // 1. this block's share of the head's approximate page scores
   select_channels_block<T, G>(q, b, h, a.Hkv, D, a.r, ch);
   if (a.chan_idx != nullptr && split == 0)
-    for (int j = tid; j < a.r; j += kThreads) a.chan_idx[(size_t)bh * a.r + j] = ch.chan[j];
+    for (int j = tid; j < a.r; j += kStepThreads) a.chan_idx[(size_t)bh * a.r + j] = ch.chan[j];
   {
     const int pb_lo = split * a.ppb1, pb_hi = min(a.P, pb_lo + a.ppb1);
     const size_t sbase = (size_t)bh * D * a.P;
@@ -434,14 +439,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     uint64_t w[E];
     bool use[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) use[j] = j * kThreads + tid < a.P;
+    for (int j = 0; j < E; ++j) use[j] = j * kStepThreads + tid < a.P;
     const uint64_t* ptr[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) ptr[j] = xs + min(j * kThreads + tid, a.P - 1);
+    for (int j = 0; j < E; ++j) ptr[j] = xs + min(j * kStepThreads + tid, a.P - 1);
     load_tagged<E>(w, use, ptr, epoch, a.sync);
 #pragma unroll
     for (int j = 0; j < E; ++j)
-      if (use[j]) s_scores[j * kThreads + tid] = tag_value(w[j]);
+      if (use[j]) s_scores[j * kStepThreads + tid] = tag_value(w[j]);
   }
   __syncthreads();
   const int p_lo = split * a.pps;
@@ -451,11 +456,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   int32_t* pout = (a.page_idx != nullptr && split == 0) ? a.page_idx + (size_t)bh * a.n_pages
                                                         : nullptr;
   if (a.n_pages >= a.P) {
-    for (int i = tid; pout != nullptr && i < a.n_pages; i += kThreads) pout[i] = i;
+    for (int i = tid; pout != nullptr && i < a.n_pages; i += kStepThreads) pout[i] = i;
     for (int w0 = p_lo; w0 < p_hi; w0 += kMaxPagesPerSplit) {
       const int nw = min(kMaxPagesPerSplit, p_hi - w0);
       __syncthreads();
-      for (int i = tid; i < nw; i += kThreads) sh.pages[i] = w0 + i;
+      for (int i = tid; i < nw; i += kStepThreads) sh.pages[i] = w0 + i;
       __syncthreads();
       st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc);
     }
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     const int i0 = tid * E;
     const int nv = load_keys<E>(s_scores, a.P, i0, key);
     uint32_t thr, need_eq;
-    block_threshold<kThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, sel);
+    block_threshold<kStepThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, sel);
     int w0 = p_lo;
     do {  // the first window also writes the full page list when asked
       const int nw = min(kMaxPagesPerSplit, max(p_hi - w0, 0));
@@ -472,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
       __syncthreads();
       const uint32_t wlo = write_out ? 0u : (uint32_t)w0;
       const uint32_t whi = write_out ? (uint32_t)a.n_pages : (uint32_t)(w0 + nw);
-      block_compact<kThreads, E>(key, nv, thr, need_eq, i0, wlo, whi, sel,
+      block_compact<kStepThreads, E>(key, nv, thr, need_eq, i0, wlo, whi, sel,
                                  [&](uint32_t pos, int idx, bool take) {
         const int p = (int)pos;
         // branch-free: elements outside the window go to the lane's spare slot
@@ -493,17 +498,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
   constexpr int kStride = G * D + 2 * G;
   uint64_t* hp = a.xpart + (size_t)bh * a.part_cap * kStride;
   if (nsa == 1) {
-    for (int idx = tid; idx < G * D; idx += kThreads) {
+    for (int idx = tid; idx < G * D; idx += kStepThreads) {
       float M, lsum, o;
-      wave_merge<D, G>(sh, idx / D, idx % D, M, lsum, o);
+      wave_merge<D, G, kStepWaves>(sh, idx / D, idx % D, M, lsum, o);
       out[idx] = from_f32<T>(lsum > 0.f ? o / lsum : 0.f);
     }
   } else {
     uint64_t* mine = hp + (size_t)split * kStride;
-    for (int idx = tid; idx < G * D; idx += kThreads) {
+    for (int idx = tid; idx < G * D; idx += kStepThreads) {
       const int g = idx / D, c = idx % D;
       float M, lsum, o;
-      wave_merge<D, G>(sh, g, c, M, lsum, o);
+      wave_merge<D, G, kStepWaves>(sh, g, c, M, lsum, o);
       st_coherent(mine + idx, tagged(o, epoch));
       if (c == 0) {
         st_coherent(mine + G * D + g, tagged(M, epoch));
@@ -527,14 +532,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     const int lne = 32 - __clz(ne - 1);  // log2 of NEP
     const int NO = nsa << lne;
     const int n_all = NO + 2 * kMaxSplit * 8;
-    for (int base = 0; base < n_all; base += kMergePer * kThreads) {
+    for (int base = 0; base < n_all; base += kMergePer * kStepThreads) {
       uint64_t w[kMergePer];
       bool use[kMergePer];
       const uint64_t* ptr[kMergePer];
       int dst[kMergePer];  // LDS slot: o index, or -1 - (which * kMaxSplit * G + s * G + gg)
 #pragma unroll
       for (int j = 0; j < kMergePer; ++j) {
-        const int i = base + j * kThreads + tid;
+        const int i = base + j * kStepThreads + tid;
         bool u_ = false;
         const uint64_t* pp = hp;
         int d = 0;
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
     }
     __syncthreads();
     if (split == 0 && tid == 0) st_coherent(epoch_word, epoch);  // every split has published
-    for (int gg = wave; gg < ng; gg += kWavesPerBlock) {  // lane = split
+    for (int gg = wave; gg < ng; gg += kStepWaves) {  // lane = split
       const float ms = lane < nsa ? mg.m[lane][gg] : -INFINITY;
       const float M = group_max<kWave>(ms);
       const float wgt = (lane < nsa && ms != -INFINITY) ? exp2_hw(ms - M) : 0.f;
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(StepArgs a) {
       if (lane == 0) mg.inv[gg] = lsum > 0.f ? 1.f / lsum : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < ne; e += kThreads) {
+    for (int e = tid; e < ne; e += kStepThreads) {
       const int gg = (e0 + e) / D - g0;
       float o = 0.f;
       for (int s = 0; s < nsa; ++s) o = fmaf(mg.o[s * ne + e], mg.m[s][gg], o);
@@ -626,9 +631,10 @@ struct StepPlan {
 template <typename T, int D>
 StepPlan plan_step(int BH, int ps, int n_pages, int ncu) {
   const int ntok = n_pages * ps;
-  const int chunk = kWavesPerBlock * Geo<T, D>::WTOK;
+  const int chunk = kStepWaves * Geo<T, D, kStepSlots>::WTOK;
   const int ns = max(min(ncu / BH, kMaxSplit), 1);
-  int na = max(min(ns, (ntok + chunk - 1) / chunk), 1);
+  // a small budget goes to one block (no partials to merge across blocks)
+  int na = ntok <= kStepSoloTokens ? 1 : max(min(ns, (ntok + chunk - 1) / chunk), 1);
   const int pps = (n_pages + na - 1) / na;
   na = (n_pages + pps - 1) / pps;
   return {ns, na, pps};
@@ -659,11 +665,11 @@ hipError_t attend_g(AttendArgs a, int BH, hipStream_t stream) {
 
 template <typename T, int D, int G>
 hipError_t step_g(StepArgs a, int BH, hipStream_t stream) {
-  if (a.P <= 16 * kThreads)
-    hipLaunchKernelGGL((k_decode_step<T, D, G, 16>), dim3(BH, a.nsplit), dim3(kThreads), 0,
+  if (a.P <= 8 * kStepThreads)
+    hipLaunchKernelGGL((k_decode_step<T, D, G, 8>), dim3(BH, a.nsplit), dim3(kStepThreads), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((k_decode_step<T, D, G, 32>), dim3(BH, a.nsplit), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_decode_step<T, D, G, 16>), dim3(BH, a.nsplit), dim3(kStepThreads), 0,
                        stream, a);
   return hipGetLastError();
 }
