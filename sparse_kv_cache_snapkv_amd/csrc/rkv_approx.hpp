@@ -25,22 +25,31 @@ struct ChannelShared {
 // thread t counts the keys of channels [64*(t/128), 64*(t/128) + 64) above channel t % 128's
 // key, and the two halves add up to its rank. Wave 0 then places the channels of rank < r in
 // ascending channel order by ballot prefix counts. The block must have at least 256 threads and
-// every thread must call both phases; phase 1 ends with a barrier, phase 2 contains two.
+// every thread must take every step: load, then phase 1 (which ends with a barrier), then phase 2
+// (two barriers). The load is separate so that a kernel can issue its other first loads before
+// any of them is waited for.
 template <typename T, int G>
-__device__ __forceinline__ void select_channels_phase1(const T* __restrict__ q, int b, int h,
-                                                       int Hkv, int D, ChannelShared& sh) {
+struct ChannelQ {
+  float x[G];  // q_g[c] of this thread's channel c = tid % kApproxMaxD (clamped into the row)
+  __device__ __forceinline__ void load(const T* __restrict__ q, int b, int h, int Hkv, int D) {
+    const int c = (int)threadIdx.x % kApproxMaxD;
+    const T* qg = q + ((size_t)b * Hkv + h) * G * D + (c < D ? c : 0);
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[g] = to_f32(qg[(size_t)g * D]);
+  }
+};
+
+template <typename T, int G>
+__device__ __forceinline__ void select_channels_phase1(const ChannelQ<T, G>& cq, int D,
+                                                       ChannelShared& sh) {
   const int tid = threadIdx.x;
   if (tid < kApproxMaxD) {
     const int c = tid;
-    const T* qg = q + ((size_t)b * Hkv + h) * G * D + (c < D ? c : 0);
-    float x[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) x[g] = to_f32(qg[(size_t)g * D]);  // all loads before any use
     float a = 0.f, sq = 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      a += fabsf(x[g]);
-      sq += x[g];
+      a += fabsf(cq.x[g]);
+      sq += cq.x[g];
     }
     // padding channels (c >= D) get key 0, below every real one
     sh.key[c] = c < D ? (((uint64_t)__float_as_uint(a) + 1ull) << 7) | (uint64_t)(127 - c) : 0ull;
@@ -87,7 +96,9 @@ __device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShar
 template <typename T, int G>
 __device__ __forceinline__ void select_channels_block(const T* __restrict__ q, int b, int h,
                                                       int Hkv, int D, int r, ChannelShared& sh) {
-  select_channels_phase1<T, G>(q, b, h, Hkv, D, sh);
+  ChannelQ<T, G> cq;
+  cq.load(q, b, h, Hkv, D);
+  select_channels_phase1<T, G>(cq, D, sh);
   select_channels_phase2(D, r, sh);
 }
 

@@ -2,11 +2,11 @@
 // a GQA group (RocketKV rebuttal, "Lack of Direct Latency Comparison": Step 3 sparse attention;
 // "Explanation of Calculating Approximate Attention Scores": one selection per group).
 //
-// Work split: block = (split of the head's page list, b*Hkv+h), 4 waves. A token row of D
-// elements is spread over LPT lanes, 16 bytes each, so one load instruction fetches TPL = 64/LPT
-// whole rows; per chunk a wave issues all its K and V loads (SLOTS of each) before reducing in
-// registers (DPP inside a row of 16 lanes), with an online softmax across chunks. The four waves
-// merge (max, sum, P.V) through LDS.
+// Work split: block = (split of the head's page list, b*Hkv+h), 4 waves (8 in the fused step). A
+// token row of D elements is spread over LPT lanes, 16 bytes each, so one load instruction
+// fetches TPL = 64/LPT whole rows; per chunk a wave issues all its K and V loads (SLOTS of each)
+// before reducing in registers (DPP inside a row of 16 lanes), with an online softmax across
+// chunks. The waves merge (max, sum, P.V) through LDS.
 //
 // The standalone call copies its slice of page_idx into LDS; several splits per head are combined
 // by k_attend_merge (log-sum-exp form). The fused decode step (k_decode_step) is one kernel:
@@ -16,8 +16,9 @@
 //      resident at once). Data that crosses blocks moves only through device-coherent loads and
 //      stores, and a tag travels in the same single-copy-atomic word as its value, so no fence
 //      or flag has to order anything;
-//   2. each attending block runs the exact block top-k (rkv_select.hpp) on all of its head's
-//      page scores and keeps its slice of the ascending page list;
+//   2. each attending block runs the exact block top-k (rkv_select.hpp, strided layout: the
+//      scores go from the exchanged words straight into registers) on all of its head's page
+//      scores and keeps its slice of the ascending page list;
 //   3. attention over that slice, published as a tagged partial (max, sum, P.V);
 //   4. every attending block merges a slice of the head's outputs over all partials, and split 0
 //      advances the head's epoch for the next call.
@@ -62,13 +63,26 @@ template <typename T, int D, int G, int NW = kWavesPerBlock, int SLOTS = kSlots>
 struct WaveState {
   float qf[G][Geo<T, D, SLOTS>::V];
   float m[G], l[G], acc[G][Geo<T, D, SLOTS>::V];
+  uint4 qraw[G];
 
-  __device__ __forceinline__ void init(const T* __restrict__ q_bh, float scale2) {
+  // The lane's slices of the G queries, as loaded; init(scale2) converts them.
+  __device__ __forceinline__ void load_q(const T* __restrict__ q_bh) {
     constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT;
     const int li = (threadIdx.x & (kWave - 1)) % LPT;
 #pragma unroll
+    for (int g = 0; g < G; ++g) qraw[g] = load16(q_bh + (size_t)g * D + li * V);
+  }
+
+  __device__ __forceinline__ void init(const T* __restrict__ q_bh, float scale2) {
+    load_q(q_bh);
+    init(scale2);
+  }
+
+  __device__ __forceinline__ void init(float scale2) {
+    constexpr int V = Geo<T, D, SLOTS>::V;
+#pragma unroll
     for (int g = 0; g < G; ++g) {
-      unpack16<T>(load16(q_bh + (size_t)g * D + li * V), qf[g]);
+      unpack16<T>(qraw[g], qf[g]);
 #pragma unroll
       for (int e = 0; e < V; ++e) qf[g][e] *= scale2;
       m[g] = -INFINITY;
@@ -379,9 +393,10 @@ constexpr int kMergePer = 8;  // tagged words a thread loads per round of the me
 template <typename T, int D, int G, int E>
 __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
   __shared__ ChannelShared ch;
-  // The head's scores are dead once the keys are in registers (block_threshold passes a barrier
-  // before any page-list or attention write), so they share LDS with the attention scratch; the
-  // merge scratch comes after the attention's last read of it.
+  // A block's own scores (single-block heads) are dead once its keys are in registers, which
+  // happens before the selection's first barrier and so before any page-list or attention write;
+  // they share LDS with the attention scratch, and the merge scratch comes after the attention's
+  // last read of it.
   __shared__ union {
     __align__(16) float scores[E * kStepThreads];
     AttendShared<D, G, kStepWaves> att;
@@ -389,7 +404,8 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
   } u;
   AttendShared<D, G, kStepWaves>& sh = u.att;
   float* s_scores = u.scores;
-  __shared__ SelectShared<kStepThreads> sel;
+  __shared__ SelectShared<kStepThreads> sel;  // the radix passes for clustered scores
+  __shared__ StridedShared<kStepThreads, E> ssel;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   // grid (BH, nsplit): consecutive blocks belong to different heads, so the round-robin
   // placement of blocks on the XCDs keeps every block of a head on one XCD when BH is a
@@ -399,17 +415,25 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
   const bool multi = a.nsplit > 1;
   const bool attends = split < a.nsplit_att;
   unsigned* epoch_word = a.sync + 16 + bh;
-  unsigned epoch = 0;
-  if (multi) {
-    epoch = ld_coherent(epoch_word) + 1u;
-    if (epoch == 0u) epoch = 1u;  // tag 0 is what a cleared workspace holds
-  }
 
-  WaveState<T, D, G, kStepWaves, kStepSlots> st;  // the queries' loads overlap the channel selection
-  if (attends) st.init(q + (size_t)bh * G * D, a.scale2);
+  // The first loads (the head's epoch word, which every workspace holds, and the queries for the
+  // attention and for the channel choice) are all issued before any of them is waited for.
+  const unsigned epoch_prev = ld_coherent(epoch_word);
+  WaveState<T, D, G, kStepWaves, kStepSlots> st;
+  st.load_q(q + (size_t)bh * G * D);
+  ChannelQ<T, G> cq;
+  cq.load(q, b, h, a.Hkv, D);
+  if (attends) strided_clear(ssel);  // ordered before its use by the channel choice's barriers
 
   // 1. this block's share of the head's approximate page scores
-  select_channels_block<T, G>(q, b, h, a.Hkv, D, a.r, ch);
+  select_channels_phase1<T, G>(cq, D, ch);
+  select_channels_phase2(D, a.r, ch);
+  unsigned epoch = 0;
+  if (multi) {
+    epoch = epoch_prev + 1u;
+    if (epoch == 0u) epoch = 1u;  // tag 0 is what a cleared workspace holds
+  }
+  if (attends) st.init(a.scale2);
   if (a.chan_idx != nullptr && split == 0)
     for (int j = tid; j < a.r; j += kStepThreads) a.chan_idx[(size_t)bh * a.r + j] = ch.chan[j];
   {
@@ -433,22 +457,26 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
   }
   if (!attends) return;  // a scoring-only block
 
-  // 2. the head's scores into LDS (coalesced), then the top pages of this block's slice
+  // 2. the top pages of the head (every attending block finds them) and this block's slice.
+  // Strided keys: thread t holds pages j * kStepThreads + t, straight from coalesced loads. In a
+  // head of several blocks every attending block reads all the scores even when it needs none of
+  // them: that wait orders every block's read of the epoch word before split 0 advances it.
+  uint32_t key[E];
+  const int nv = tid < a.P ? min(E, (a.P - 1 - tid) / kStepThreads + 1) : 0;
   if (multi) {
     const uint64_t* xs = a.xscores + (size_t)bh * a.P;
     uint64_t w[E];
     bool use[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) use[j] = j * kStepThreads + tid < a.P;
     const uint64_t* ptr[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) ptr[j] = xs + min(j * kStepThreads + tid, a.P - 1);
+    for (int j = 0; j < E; ++j) {
+      use[j] = j < nv;
+      ptr[j] = xs + min(j * kStepThreads + tid, a.P - 1);
+    }
     load_tagged<E>(w, use, ptr, epoch, a.sync);
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-      if (use[j]) s_scores[j * kStepThreads + tid] = tag_value(w[j]);
+    for (int j = 0; j < E; ++j) key[j] = use[j] ? order_key(tag_value(w[j])) : 0u;
   }
-  __syncthreads();
   const int p_lo = split * a.pps;
   const int p_hi = min(p_lo + a.pps, a.n_pages);
   const T* kc_bh = static_cast<const T*>(a.k_c) + (size_t)bh * a.Lc * D;
@@ -465,25 +493,29 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
       st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc);
     }
   } else {
-    uint32_t key[E];
-    const int i0 = tid * E;
-    const int nv = load_keys<E>(s_scores, a.P, i0, key);
+    if (!multi) {
+      __syncthreads();  // the block's own scores are in LDS
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        key[j] = j < nv ? order_key(s_scores[min(j * kStepThreads + tid, a.P - 1)]) : 0u;
+    }
     uint32_t thr, need_eq;
-    block_threshold<kStepThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, sel);
+    strided_threshold<kStepThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, ssel, sel);
+    uint32_t pos[E], take;
+    strided_positions<kStepThreads, E>(key, nv, thr, need_eq, ssel, pos, take);
     int w0 = p_lo;
     do {  // the first window also writes the full page list when asked
       const int nw = min(kMaxPagesPerSplit, max(p_hi - w0, 0));
       const bool write_out = pout != nullptr && w0 == p_lo;
-      __syncthreads();
-      const uint32_t wlo = write_out ? 0u : (uint32_t)w0;
-      const uint32_t whi = write_out ? (uint32_t)a.n_pages : (uint32_t)(w0 + nw);
-      block_compact<kStepThreads, E>(key, nv, thr, need_eq, i0, wlo, whi, sel,
-                                 [&](uint32_t pos, int idx, bool take) {
-        const int p = (int)pos;
-        // branch-free: elements outside the window go to the lane's spare slot
-        sh.pages[(take && p >= w0 && p < w0 + nw) ? p - w0 : kMaxPagesPerSplit + lane] = idx;
-        if (write_out && take && p < a.n_pages) pout[p] = idx;
-      });
+      if (w0 != p_lo) __syncthreads();  // the previous window's attention has read its pages
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        if ((take >> j) & 1u) {
+          const int p = (int)pos[j], idx = j * kStepThreads + tid;
+          if (p >= w0 && p < w0 + nw) sh.pages[p - w0] = idx;
+          if (write_out && p < a.n_pages) pout[p] = idx;
+        }
+      }
       __syncthreads();
       st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc);
       w0 += kMaxPagesPerSplit;

@@ -320,4 +320,261 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ row, int n, i
   return n - i0 < 0 ? 0 : (n - i0 > E ? E : n - i0);
 }
 
+// ------------------------------------------------------------------------- strided layout
+// Thread t of a block of THREADS threads holds elements j*THREADS + t (j < E) of a row as keys;
+// the valid ones are j < nvalid (a prefix, since the row end cuts every thread's j range). The
+// keys come straight from coalesced loads, and the per-element work uses wave ballots where the
+// blocked layout above needs block scans: the bin holding the k-th largest key is found by every
+// wave from the per-wave totals, its keys are ranked by every wave, and positions come from a
+// table of per-(j, wave) counts, so a selection passes four barriers and the positions one.
+
+constexpr int kStridedCandidates = 256;  // bin size up to which the bin's keys are ranked directly
+
+template <int THREADS, int E>
+struct StridedShared {
+  static constexpr int NW = THREADS / kWave;
+  static constexpr int NTAB = E * NW;  // (j, wave) groups in index order
+  uint32_t vbins[kValueBins];
+  __align__(16) uint32_t cand[kStridedCandidates + 4];
+  uint32_t wmin[NW], wmax[NW], wtot[NW];
+  uint32_t ncand;
+  uint32_t gtc[NTAB], eqc[NTAB];
+};
+
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+}
+
+// Zeroes what strided_threshold expects to be zero; the block must pass a barrier afterwards.
+template <int THREADS, int E>
+__device__ __forceinline__ void strided_clear(StridedShared<THREADS, E>& sh) {
+  for (int i = threadIdx.x; i < kValueBins; i += THREADS) sh.vbins[i] = 0u;
+  if (threadIdx.x == 0) sh.ncand = 0u;
+}
+
+// T (the k-th largest key) and need_eq (how many keys equal to T are taken), for 1 <= k < number
+// of valid keys, with sh cleared by strided_clear (and a barrier passed) since its last use.
+// Value-linear bins between the block's minimum and maximum locate the bin of the k-th largest
+// key; a bin of at most kStridedCandidates keys is gathered and ranked, larger ones (clustered
+// values) go to block_threshold's radix passes in fb. Every thread must call it.
+template <int THREADS, int E>
+__device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int nvalid, uint32_t k,
+                                                  uint32_t& T, uint32_t& need_eq,
+                                                  StridedShared<THREADS, E>& sh,
+                                                  SelectShared<THREADS>& fb) {
+  constexpr int NW = THREADS / kWave;
+  constexpr int BPT = kValueBins / THREADS;
+  static_assert(BPT % 4 == 0, "bins per thread");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    lo = e < nvalid ? min(lo, key[e]) : lo;
+    hi = e < nvalid ? max(hi, key[e]) : hi;
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    sh.wmin[wave] = lo;
+    sh.wmax[wave] = hi;
+  }
+  __syncthreads();
+  lo = sh.wmin[0];
+  hi = sh.wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    lo = min(lo, sh.wmin[w]);
+    hi = max(hi, sh.wmax[w]);
+  }
+  if (lo == hi) {  // all keys equal
+    T = lo;
+    need_eq = k;
+    return;
+  }
+  const float flo = key_float(lo), fhi = key_float(hi);
+  const float inv = (float)kValueBins / (fhi - flo);
+  if (isfinite(flo) && isfinite(fhi) && isfinite(inv) && inv > 0.f) {
+    int bin[E];  // a monotone function of the key
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      bin[e] = min(max((int)((key_float(key[e]) - flo) * inv), 0), kValueBins - 1);
+      if (e < nvalid) atomicAdd(&sh.vbins[bin[e]], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins kValueBins-1-(t*BPT+i), i < BPT (descending from the top)
+    auto read_bins = [&](int t, uint32_t (&c)[BPT]) {
+#pragma unroll
+      for (int i = 0; i < BPT; i += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sh.vbins[kValueBins - (t * BPT + i) - 4]);
+        c[i] = v.w;
+        c[i + 1] = v.z;
+        c[i + 2] = v.y;
+        c[i + 3] = v.x;
+      }
+    };
+    uint32_t c[BPT], local = 0;
+    read_bins(tid, c);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) local += c[i];
+    const uint32_t incl = wave_inclusive_scan(local);
+    if (lane == kWave - 1) sh.wtot[wave] = incl;
+    __syncthreads();
+    // the wave whose bins reach the k-th key, then (in every wave) the bin within it
+    uint32_t before = 0, wabove = 0;
+    int wstar = 0;
+    bool found = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t t = sh.wtot[w];
+      const bool here = !found && k <= before + t;
+      wstar = here ? w : wstar;
+      wabove = here ? before : wabove;
+      found = found || here;
+      before += t;
+    }
+    uint32_t cw[BPT], lw = 0;
+    read_bins(wstar * kWave + lane, cw);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) lw += cw[i];
+    uint32_t run = wabove + wave_inclusive_scan(lw) - lw;
+    int bsel = 0;
+    uint32_t asel = 0, csel = 0;
+    bool has = false;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const bool here = !has && run < k && k <= run + cw[i];
+      bsel = here ? kValueBins - 1 - ((wstar * kWave + lane) * BPT + i) : bsel;
+      asel = here ? run : asel;
+      csel = here ? cw[i] : csel;
+      has = has || here;
+      run += cw[i];
+    }
+    const int src = __ffsll((long long)__ballot(has)) - 1;
+    const int bstar = __builtin_amdgcn_readlane(bsel, src);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)asel, src);
+    const uint32_t nbin = (uint32_t)__builtin_amdgcn_readlane((int)csel, src);
+    if (nbin <= (uint32_t)kStridedCandidates) {
+      bool m[E];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        m[e] = e < nvalid && bin[e] == bstar;
+        cnt += m[e] ? 1u : 0u;
+      }
+      const uint32_t wincl = wave_inclusive_scan(cnt);
+      uint32_t base = 0;
+      if (lane == kWave - 1 && wincl != 0u) base = atomicAdd(&sh.ncand, wincl);
+      base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1);
+      uint32_t slot = base + wincl - cnt;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (m[e]) sh.cand[slot] = key[e];
+        slot += m[e] ? 1u : 0u;
+      }
+      __syncthreads();
+      // every wave ranks the bin's keys (lane l: keys l, l+64, ...) against each other
+      const uint32_t krem = k - above;
+      uint32_t tsel = 0, nsel = 0;
+      bool ok = false;
+      for (uint32_t i0 = 0; i0 < nbin; i0 += kWave) {
+        const uint32_t ci = i0 + lane;
+        const uint32_t kt = sh.cand[min(ci, nbin - 1)];
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t j = 0; j < nbin; j += 4) {
+          const uint4 c4 = *reinterpret_cast<const uint4*>(&sh.cand[j]);
+          gt += (c4.x > kt) + (j + 1 < nbin && c4.y > kt) + (j + 2 < nbin && c4.z > kt) +
+                (j + 3 < nbin && c4.w > kt);
+          ge += (c4.x >= kt) + (j + 1 < nbin && c4.y >= kt) + (j + 2 < nbin && c4.z >= kt) +
+                (j + 3 < nbin && c4.w >= kt);
+        }
+        const bool here = ci < nbin && gt < krem && krem <= ge;  // kt is the krem-th largest
+        tsel = here ? kt : tsel;
+        nsel = here ? krem - gt : nsel;
+        ok = ok || here;
+      }
+      const int s2 = __ffsll((long long)__ballot(ok)) - 1;
+      T = (uint32_t)__builtin_amdgcn_readlane((int)tsel, s2);
+      need_eq = (uint32_t)__builtin_amdgcn_readlane((int)nsel, s2);
+      return;
+    }
+  }
+  block_threshold<THREADS, E>(key, nvalid, k, T, need_eq, fb);
+}
+
+// Ascending positions of the selected elements: the elements above T and the need_eq
+// lowest-index elements equal to T. pos[e] is meaningful where bit e of take is set. One
+// barrier; every thread must call it.
+template <int THREADS, int E>
+__device__ __forceinline__ void strided_positions(const uint32_t (&key)[E], int nvalid, uint32_t T,
+                                                  uint32_t need_eq, StridedShared<THREADS, E>& sh,
+                                                  uint32_t (&pos)[E], uint32_t& take) {
+  constexpr int NW = THREADS / kWave;
+  constexpr int NTAB = E * NW;
+  constexpr int R = (NTAB + kWave - 1) / kWave;  // table entries per lane
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  uint64_t bg[E], be[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    bg[e] = __ballot(e < nvalid && key[e] > T);
+    be[e] = __ballot(e < nvalid && key[e] == T);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sh.gtc[e * NW + wave] = (uint32_t)__popcll(bg[e]);
+      sh.eqc[e * NW + wave] = (uint32_t)__popcll(be[e]);
+    }
+  }
+  __syncthreads();
+  // every wave scans the table: lane l holds entries l*R .. l*R+R-1
+  uint32_t tg[R], te[R], le = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int en = lane * R + r;
+    tg[r] = en < NTAB ? sh.gtc[en] : 0u;
+    te[r] = en < NTAB ? sh.eqc[en] : 0u;
+    le += te[r];
+  }
+  uint32_t run = wave_inclusive_scan(le) - le;  // keys equal to T in earlier entries
+  uint32_t eqx[R], tk[R], lt = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    eqx[r] = run;
+    tk[r] = tg[r] + min(te[r], need_eq > run ? need_eq - run : 0u);
+    run += te[r];
+    lt += tk[r];
+  }
+  uint32_t bs[R];
+  run = wave_inclusive_scan(lt) - lt;  // selected elements in earlier entries
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    bs[r] = run;
+    run += tk[r];
+  }
+  take = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int en = e * NW + wave;
+    const int src = en / R, sub = en % R;
+    uint32_t b0 = 0, x0 = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t vb = (uint32_t)__builtin_amdgcn_readlane((int)bs[r], src);
+      const uint32_t vx = (uint32_t)__builtin_amdgcn_readlane((int)eqx[r], src);
+      b0 = r == sub ? vb : b0;
+      x0 = r == sub ? vx : x0;
+    }
+    const bool gt = e < nvalid && key[e] > T;
+    const bool eq = e < nvalid && key[e] == T;
+    const bool tk_e = gt || (eq && x0 + lanes_below(be[e]) < need_eq);
+    pos[e] = b0 + lanes_below(__ballot(tk_e));
+    take |= tk_e ? (1u << e) : 0u;
+  }
+}
+
 }  // namespace rkv

@@ -350,6 +350,64 @@ def test_fused_decode_step_windows_one_block_per_head(rkv):
         assert_rows_close(got[b, h:h + 1], ref, TOL_OUT["bf16"], f"b{b} h{h}")
 
 
+def _check_fused_heads(rkv, w, q, k_c, v_c, topk, heads, scale):
+    kmin, kmax = rkv.rkv_build_page_summaries(k_c, w.page_size)
+    out, pages, _ = _fused_vs_calls(rkv, w, q, k_c, v_c, kmin, kmax, topk)
+    got, pg = O.widen(H(out)), pages.cpu().numpy()
+    q64 = O.widen(H(q))
+    G = w.Hq // w.Hkv
+    for (b, h) in heads:
+        toks = O.page_tokens(pg[b, h], w.page_size, w.Lc)
+        ref = O.sparse_attention(q64[b, h * G:(h + 1) * G], O.widen(H(k_c[b, h])),
+                                 O.widen(H(v_c[b, h])), toks, scale)
+        assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT["bf16"], f"b{b} h{h} k{topk}")
+
+
+def test_fused_decode_step_rows_over_4096_pages(rkv):
+    # a head spread over many blocks, with more pages than 8 per thread of a block
+    w = configs.SMALL[1].replace(name="p6000", B=1, Hq=4, Hkv=2, D=64, L=6000, keep=6000,
+                                 page_size=1, r=16, cfg_id=41)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    k_c = torch.randn((w.B, w.Hkv, w.Lc, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    v_c = torch.randn((w.B, w.Hkv, w.Lc, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn((w.B, w.Hq, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    for topk in (1, 64, 3000, 5999):
+        _check_fused_heads(rkv, w, q, k_c, v_c, topk, [(0, 0), (0, 1)], 0.125)
+
+
+def _tied_keys(B, Hkv, P, ps, D, mode, seed):
+    """K caches whose pages repeat, so that page scores tie exactly: every page the same, half
+    of the pages the same, or pages in groups of three."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, Hkv, P, ps, D)).astype(np.float32)
+    if mode == "all":
+        k[:] = k[:, :, :1]
+    elif mode == "half":
+        sel = rng.permutation(P)[: P // 2]
+        k[:, :, sel] = k[:, :, sel[:1]]
+    elif mode == "triples":
+        k = k[:, :, (np.arange(P) // 3) * 3]
+    return torch.from_numpy(np.ascontiguousarray(k).reshape(B, Hkv, P * ps, D)).to(
+        "cuda", torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", ["all", "half", "triples"])
+@pytest.mark.parametrize("B,P", [(1, 4096), (128, 256)], ids=["many-blocks", "one-block"])
+def test_fused_decode_step_tied_scores(rkv, mode, B, P):
+    # exact ties in the page scores: the lower page index wins in the fused step as in the
+    # separate top-k call (all equal, a crowded bin, and small tied groups)
+    ps, D = 4, 128
+    w = configs.SMALL[1].replace(name=f"ties-{mode}", B=B, Hq=8, Hkv=2, D=D, L=P * ps,
+                                 keep=P * ps, page_size=ps, r=32, cfg_id=42)
+    k_c = _tied_keys(B, w.Hkv, P, ps, D, mode, 5)
+    g = torch.Generator(device="cuda").manual_seed(6)
+    v_c = torch.randn((B, w.Hkv, w.Lc, D), device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn((B, w.Hq, D), device="cuda", generator=g).to(torch.bfloat16)
+    heads = [(0, 0), (B - 1, 1)]
+    for n in (1, P // 4, P // 2, 3 * P // 4, P - 1):
+        _check_fused_heads(rkv, w, q, k_c, v_c, n * ps, heads, 1 / math.sqrt(D))
+
+
 def test_fused_decode_step_graph_replays(rkv):
     w = configs.SMALL[1]
     wc, d, qs = _cache(w, steps=3)
