@@ -3,8 +3,8 @@
 // Approximate Attention Scores"; "Novelty": reduction along sequence and head dims).
 //
 // Block = (page range, b*Hkv+h): the block ranks the group's channels (a few hundred bytes of q,
-// cache resident); then each quad of lanes scores one 16-byte vector of consecutive pages, each
-// lane summing a quarter of the chosen channels with all of its loads in flight, and only the
+// cache resident); then each row of 16 lanes scores one 16-byte vector of consecutive pages, each
+// lane summing a sixteenth of the chosen channels with all of its loads in flight, and only the
 // Kmin or the Kmax row of each channel is read. The fused decode step uses the same device
 // functions, so both produce identical scores.
 #include "rkv_approx.hpp"

@@ -58,12 +58,16 @@ struct AttendShared {
 };
 
 // Per-wave online-softmax state of the G heads of a group; NW waves share a block's page list and
-// each issues SLOTS K and V row loads per chunk.
+// each issues SLOTS K and V row loads per chunk. bf16 scores are packed bf16 dot products of the
+// raw query and key bits, scaled after the lane reduction; fp32 scores use the pre-scaled query.
 template <typename T, int D, int G, int NW = kWavesPerBlock, int SLOTS = kSlots>
 struct WaveState {
-  float qf[G][Geo<T, D, SLOTS>::V];
+  static constexpr bool kBf16 = elem<T>::bytes == 2;
+  float qf[G][Geo<T, D, SLOTS>::V];  // fp32 only: the query times scale * log2(e)
   float m[G], l[G], acc[G][Geo<T, D, SLOTS>::V];
   uint4 qraw[G];
+  float sc2;     // scale * log2(e)
+  bool started;  // a chunk has been accumulated (before it, rescaling zeros is skipped)
 
   // The lane's slices of the G queries, as loaded; init(scale2) converts them.
   __device__ __forceinline__ void load_q(const T* __restrict__ q_bh) {
@@ -80,11 +84,15 @@ struct WaveState {
 
   __device__ __forceinline__ void init(float scale2) {
     constexpr int V = Geo<T, D, SLOTS>::V;
+    sc2 = scale2;
+    started = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      unpack16<T>(qraw[g], qf[g]);
+      if constexpr (!kBf16) {
+        unpack16<T>(qraw[g], qf[g]);
 #pragma unroll
-      for (int e = 0; e < V; ++e) qf[g][e] *= scale2;
+        for (int e = 0; e < V; ++e) qf[g][e] *= scale2;
+      }
       m[g] = -INFINITY;
       l[g] = 0.f;
 #pragma unroll
@@ -121,20 +129,33 @@ struct WaveState {
         vr[s] = load16_stream(vb + (size_t)tok[s] * D);
       }
       float sc[SLOTS][G];
+      if constexpr (kBf16) {
+        float d[SLOTS * G];
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        float kf[V];
-        unpack16<T>(kr[s], kf);
+        for (int s = 0; s < SLOTS; ++s)
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
+          for (int g = 0; g < G; ++g) d[s * G + g] = dot8_bf16(qraw[g], kr[s]);
+        group_sum_n<LPT>(d);
 #pragma unroll
-          for (int e = 0; e < V; ++e) d = fmaf(qf[g][e], kf[e], d);
-          d = group_sum<LPT>(d);
-          sc[s][g] = ok[s] ? d : -INFINITY;
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+          for (int g = 0; g < G; ++g) sc[s][g] = ok[s] ? d[s * G + g] * sc2 : -INFINITY;
+      } else {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+          float kf[V];
+          unpack16<T>(kr[s], kf);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) d = fmaf(qf[g][e], kf[e], d);
+            d = group_sum<LPT>(d);
+            sc[s][g] = ok[s] ? d : -INFINITY;
+          }
         }
       }
-      float mu[G];
+      float mu[G], f[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float x = sc[0][g];
@@ -142,13 +163,20 @@ struct WaveState {
         for (int s = 1; s < SLOTS; ++s) x = fmaxf(x, sc[s][g]);
         x = across_max<LPT>(x);
         const float mn = fmaxf(m[g], x);
-        const float f = mn == -INFINITY ? 1.f : exp2_hw(m[g] - mn);
+        f[g] = mn == -INFINITY ? 1.f : exp2_hw(m[g] - mn);
         mu[g] = mn == -INFINITY ? 0.f : mn;
         m[g] = mn;
-        l[g] *= f;
-#pragma unroll
-        for (int e = 0; e < V; ++e) acc[g][e] *= f;
       }
+      // `started` is the same in every lane; until the first chunk, l and acc are zero
+      if (__builtin_amdgcn_readfirstlane((int)started)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          l[g] *= f[g];
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[g][e] *= f[g];
+        }
+      }
+      started = true;
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         float vf[V];
@@ -499,10 +527,12 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
       for (int j = 0; j < E; ++j)
         key[j] = j < nv ? order_key(s_scores[min(j * kStepThreads + tid, a.P - 1)]) : 0u;
     }
-    uint32_t thr, need_eq;
-    strided_threshold<kStepThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, ssel, sel);
+    uint32_t thr, need_eq, eq_total;
+    strided_threshold<kStepThreads, E>(key, nv, (uint32_t)a.n_pages, thr, need_eq, eq_total,
+                                       ssel, sel);
     uint32_t pos[E], take;
-    strided_positions<kStepThreads, E>(key, nv, thr, need_eq, ssel, pos, take);
+    strided_positions<kStepThreads, E>(key, nv, thr, need_eq, eq_total == need_eq, ssel, pos,
+                                       take);
     int w0 = p_lo;
     do {  // the first window also writes the full page list when asked
       const int nw = min(kMaxPagesPerSplit, max(p_hi - w0, 0));

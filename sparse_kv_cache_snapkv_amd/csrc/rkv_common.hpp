@@ -79,6 +79,19 @@ __device__ __forceinline__ void unpack16<bf16_t>(const uint4& raw, float (&out)[
   out[7] = __uint_as_float(raw.w & 0xffff0000u);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Dot product of two 16-byte vectors of bf16 (8 elements) by the gfx950 packed bf16 dot
+// instruction, pairs (x, y, z, w) in turn, accumulated in fp32; every bf16 product is exact in
+// fp32.
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
+  auto p = [](uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); };
+  float d = __builtin_amdgcn_fdot2_f32_bf16(p(a.x), p(b.x), 0.f, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(p(a.y), p(b.y), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(p(a.z), p(b.z), d, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(p(a.w), p(b.w), d, false);
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -166,6 +179,27 @@ __device__ __forceinline__ float group_reduce(float v, Op op) {
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
   return group_reduce<width>(v, OpSum{});
+}
+
+// group_sum of N values at once, one reduction level across all of them before the next, so
+// that no DPP read waits on the write just before it.
+template <int width, int N>
+__device__ __forceinline__ void group_sum_n(float (&v)[N]) {
+  static_assert(width <= 16, "row-local widths");
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<kDppXor1>(v[i]);
+  if constexpr (width >= 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<kDppXor2>(v[i]);
+  }
+  if constexpr (width >= 8) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<kDppHalfMirror>(v[i]);
+  }
+  if constexpr (width >= 16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<kDppMirror>(v[i]);
+  }
 }
 template <int width>
 __device__ __forceinline__ float group_max(float v) {

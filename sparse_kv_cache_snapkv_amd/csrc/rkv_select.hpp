@@ -357,14 +357,16 @@ __device__ __forceinline__ void strided_clear(StridedShared<THREADS, E>& sh) {
   if (threadIdx.x == 0) sh.ncand = 0u;
 }
 
-// T (the k-th largest key) and need_eq (how many keys equal to T are taken), for 1 <= k < number
-// of valid keys, with sh cleared by strided_clear (and a barrier passed) since its last use.
+// T (the k-th largest key), need_eq (how many keys equal to T are taken) and eq_total (how many
+// keys equal T, or 0xffffffff where the radix passes leave it uncounted), for 1 <= k < number of
+// valid keys, with sh cleared by strided_clear (and a barrier passed) since its last use.
 // Value-linear bins between the block's minimum and maximum locate the bin of the k-th largest
 // key; a bin of at most kStridedCandidates keys is gathered and ranked, larger ones (clustered
 // values) go to block_threshold's radix passes in fb. Every thread must call it.
 template <int THREADS, int E>
 __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int nvalid, uint32_t k,
                                                   uint32_t& T, uint32_t& need_eq,
+                                                  uint32_t& eq_total,
                                                   StridedShared<THREADS, E>& sh,
                                                   SelectShared<THREADS>& fb) {
   constexpr int NW = THREADS / kWave;
@@ -394,6 +396,7 @@ __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int 
   if (lo == hi) {  // all keys equal
     T = lo;
     need_eq = k;
+    eq_total = 0xffffffffu;
     return;
   }
   const float flo = key_float(lo), fhi = key_float(hi);
@@ -479,7 +482,7 @@ __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int 
       __syncthreads();
       // every wave ranks the bin's keys (lane l: keys l, l+64, ...) against each other
       const uint32_t krem = k - above;
-      uint32_t tsel = 0, nsel = 0;
+      uint32_t tsel = 0, nsel = 0, esel = 0;
       bool ok = false;
       for (uint32_t i0 = 0; i0 < nbin; i0 += kWave) {
         const uint32_t ci = i0 + lane;
@@ -495,28 +498,81 @@ __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int 
         const bool here = ci < nbin && gt < krem && krem <= ge;  // kt is the krem-th largest
         tsel = here ? kt : tsel;
         nsel = here ? krem - gt : nsel;
+        esel = here ? ge - gt : esel;  // every key equal to T is in this bin
         ok = ok || here;
       }
       const int s2 = __ffsll((long long)__ballot(ok)) - 1;
       T = (uint32_t)__builtin_amdgcn_readlane((int)tsel, s2);
       need_eq = (uint32_t)__builtin_amdgcn_readlane((int)nsel, s2);
+      eq_total = (uint32_t)__builtin_amdgcn_readlane((int)esel, s2);
       return;
     }
   }
   block_threshold<THREADS, E>(key, nvalid, k, T, need_eq, fb);
+  eq_total = 0xffffffffu;
 }
 
 // Ascending positions of the selected elements: the elements above T and the need_eq
-// lowest-index elements equal to T. pos[e] is meaningful where bit e of take is set. One
-// barrier; every thread must call it.
+// lowest-index elements equal to T. pos[e] is meaningful where bit e of take is set. all_eq
+// (block-uniform): every key equal to T is taken (need_eq equals their count), so no element's
+// rank among the equal keys is needed. One barrier; every thread must call it.
 template <int THREADS, int E>
 __device__ __forceinline__ void strided_positions(const uint32_t (&key)[E], int nvalid, uint32_t T,
-                                                  uint32_t need_eq, StridedShared<THREADS, E>& sh,
+                                                  uint32_t need_eq, bool all_eq,
+                                                  StridedShared<THREADS, E>& sh,
                                                   uint32_t (&pos)[E], uint32_t& take) {
   constexpr int NW = THREADS / kWave;
   constexpr int NTAB = E * NW;
   constexpr int R = (NTAB + kWave - 1) / kWave;  // table entries per lane
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  // base[e]: selected elements of the table entries (j, w) before entry (e, wave), in index order
+  auto bases = [&](const uint32_t (&tk)[R], uint32_t (&b)[E]) {
+    uint32_t lt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) lt += tk[r];
+    uint32_t bs[R], run = wave_inclusive_scan(lt) - lt;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      bs[r] = run;
+      run += tk[r];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int en = e * NW + wave;
+      uint32_t v = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)bs[r], en / R);
+        v = r == en % R ? x : v;
+      }
+      b[e] = v;
+    }
+  };
+  uint32_t b[E];
+  take = 0u;
+  if (all_eq) {
+    uint64_t bt[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) bt[e] = __ballot(e < nvalid && key[e] >= T);
+    if (lane == 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sh.gtc[e * NW + wave] = (uint32_t)__popcll(bt[e]);
+    }
+    __syncthreads();
+    uint32_t tk[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int en = lane * R + r;
+      tk[r] = en < NTAB ? sh.gtc[en] : 0u;
+    }
+    bases(tk, b);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      pos[e] = b[e] + lanes_below(bt[e]);
+      take |= (e < nvalid && key[e] >= T) ? (1u << e) : 0u;
+    }
+    return;
+  }
   uint64_t bg[E], be[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -541,38 +597,27 @@ __device__ __forceinline__ void strided_positions(const uint32_t (&key)[E], int 
     le += te[r];
   }
   uint32_t run = wave_inclusive_scan(le) - le;  // keys equal to T in earlier entries
-  uint32_t eqx[R], tk[R], lt = 0;
+  uint32_t eqx[R], tk[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     eqx[r] = run;
     tk[r] = tg[r] + min(te[r], need_eq > run ? need_eq - run : 0u);
     run += te[r];
-    lt += tk[r];
   }
-  uint32_t bs[R];
-  run = wave_inclusive_scan(lt) - lt;  // selected elements in earlier entries
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    bs[r] = run;
-    run += tk[r];
-  }
-  take = 0u;
+  bases(tk, b);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int en = e * NW + wave;
-    const int src = en / R, sub = en % R;
-    uint32_t b0 = 0, x0 = 0;
+    uint32_t x0 = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint32_t vb = (uint32_t)__builtin_amdgcn_readlane((int)bs[r], src);
-      const uint32_t vx = (uint32_t)__builtin_amdgcn_readlane((int)eqx[r], src);
-      b0 = r == sub ? vb : b0;
-      x0 = r == sub ? vx : x0;
+      const uint32_t vx = (uint32_t)__builtin_amdgcn_readlane((int)eqx[r], en / R);
+      x0 = r == en % R ? vx : x0;
     }
     const bool gt = e < nvalid && key[e] > T;
     const bool eq = e < nvalid && key[e] == T;
     const bool tk_e = gt || (eq && x0 + lanes_below(be[e]) < need_eq);
-    pos[e] = b0 + lanes_below(__ballot(tk_e));
+    pos[e] = b[e] + lanes_below(__ballot(tk_e));
     take |= tk_e ? (1u << e) : 0u;
   }
 }
