@@ -370,12 +370,10 @@ __device__ __forceinline__ bool tag_is(uint64_t w, unsigned epoch) {
 }
 __device__ __forceinline__ float tag_value(uint64_t w) { return __uint_as_float((unsigned)w); }
 
-// Loads N tagged words (addr(j) for j with use(j)) until every tag is `epoch`. After the first
-// attempt a waiting wave re-reads a single word per poll (the first stale word of its lowest lane
-// that has one, read by every lane at once) and reloads its stale words only once that word has
-// turned current, so the waiting readers of a whole grid add little traffic. Bounded: on give-up
-// the status word is set and the stale values are used. Call with the whole wave (the exit is
-// wave-uniform).
+// Loads N tagged words (addr(j) for j with use(j)) until every tag is `epoch`: a waiting wave
+// re-reads only its stale words, after a short sleep, so a word is seen one L2 round trip after
+// it lands. Bounded: on give-up the status word is set and the stale values are used. Call with
+// the whole wave (the exit is wave-uniform).
 template <int N>
 __device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[N],
                                             const uint64_t* const (&ptr)[N], unsigned epoch,
@@ -383,28 +381,18 @@ __device__ __forceinline__ void load_tagged(uint64_t (&w)[N], const bool (&use)[
 #pragma unroll
   for (int j = 0; j < N; ++j) w[j] = use[j] ? ld_coherent(ptr[j]) : 0ull;
   for (int polls = 0;; ++polls) {
-    const uint64_t* first_stale = nullptr;
+    bool stale = false;
 #pragma unroll
-    for (int j = N - 1; j >= 0; --j)
-      if (use[j] && !tag_is(w[j], epoch)) first_stale = ptr[j];
-    const uint64_t waiting = __ballot(first_stale != nullptr);
-    if (waiting == 0ull) return;
+    for (int j = 0; j < N; ++j) stale = stale || (use[j] && !tag_is(w[j], epoch));
+    if (__ballot(stale) == 0ull) return;
     if (polls > kSpinLimit) {
-      if (first_stale != nullptr)
-        __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (stale) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
-    const int src = __ffsll((long long)waiting) - 1;
-    const uint64_t pa = (uint64_t)(uintptr_t)first_stale;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pa, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pa >> 32), src);
-    const uint64_t* probe = reinterpret_cast<const uint64_t*>(((uint64_t)hi << 32) | lo);
-    __builtin_amdgcn_s_sleep(2);
-    if (tag_is(ld_coherent(probe), epoch)) {
+    __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-      for (int j = 0; j < N; ++j)
-        if (use[j] && !tag_is(w[j], epoch)) w[j] = ld_coherent(ptr[j]);
-    }
+    for (int j = 0; j < N; ++j)
+      if (use[j] && !tag_is(w[j], epoch)) w[j] = ld_coherent(ptr[j]);
   }
 }
 
