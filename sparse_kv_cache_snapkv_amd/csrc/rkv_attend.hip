@@ -329,6 +329,8 @@ constexpr int kStepThreads = 512;  // threads of a fused-step block: two waves p
 constexpr int kStepWaves = kStepThreads / kWave;
 constexpr int kStepSlots = 4;       // row loads per wave per chunk in the fused step
 constexpr int kStepSoloTokens = 128;  // budgets up to this many tokens: one attending block
+constexpr int kStepTokensPerBlock = 64;  // attending blocks: one per this many budget tokens,
+constexpr int kMaxAttending = 16;        // at most this many per head (each reads every score)
 
 // Cross-block data of the fused step is exchanged as 64-bit words {value bits, epoch}: every
 // block of a head reads the head's epoch word at the start, tags what it publishes with
@@ -681,10 +683,11 @@ struct StepPlan {
 template <typename T, int D>
 StepPlan plan_step(int BH, int ps, int n_pages, int ncu) {
   const int ntok = n_pages * ps;
-  const int chunk = kStepWaves * Geo<T, D, kStepSlots>::WTOK;
+  const int chunk = kStepTokensPerBlock;
   const int ns = max(min(ncu / BH, kMaxSplit), 1);
   // a small budget goes to one block (no partials to merge across blocks)
-  int na = ntok <= kStepSoloTokens ? 1 : max(min(ns, (ntok + chunk - 1) / chunk), 1);
+  int na = ntok <= kStepSoloTokens ? 1
+                                   : max(min(min(ns, kMaxAttending), (ntok + chunk - 1) / chunk), 1);
   const int pps = (n_pages + na - 1) / na;
   na = (n_pages + pps - 1) / pps;
   return {ns, na, pps};
