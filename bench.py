@@ -317,6 +317,53 @@ def main() -> int:
         print(f"warning: a fused decode step reported a synchronisation timeout {status}",
               file=sys.stderr)
 
+    # ---- outside the timed region: a cache that grows during decoding (replica 0's compressed
+    # layer copied into caches of capacity Lc + nsteps): one append per step, then the same
+    # appends each followed by the fused step on the grown cache (smallest top-k)
+    cap = Lc + nsteps
+    kc_g = torch.zeros((B, Hkv, cap, D), dtype=dt, device=dev)
+    vc_g = torch.zeros_like(kc_g)
+    kc_g[:, :, :Lc] = k_c[0]
+    vc_g[:, :, :Lc] = v_c[0]
+    kmin_g, kmax_g = rkv.rkv_build_page_summaries_cap(kc_g, Lc, w.page_size)
+    gg = torch.Generator(device=dev).manual_seed(1)
+    k_new = torch.randn((nsteps, B, Hkv, D), device=dev, generator=gg).to(dt)
+    v_new = torch.randn((nsteps, B, Hkv, D), device=dev, generator=gg).to(dt)
+    tk_g = w.topk[0]
+    ws_g = rkv.rkv_hybrid_decode_workspace(q_dec[0], Hkv, cap, w.page_size, n_pages[tk_g])
+
+    def append_all():
+        for s in range(nsteps):
+            rkv.rkv_kv_append(k_new[s], v_new[s], kc_g, vc_g, kmin_g, kmax_g, Lc + s, w.page_size)
+
+    def grow_all():
+        for s in range(nsteps):
+            rkv.rkv_kv_append(k_new[s], v_new[s], kc_g, vc_g, kmin_g, kmax_g, Lc + s, w.page_size)
+            rkv.rkv_hybrid_decode_step_cap(q_dec[s], kmin_g, kmax_g, kc_g, vc_g, Lc + s + 1,
+                                           w.page_size, w.r, n_pages[tk_g], scale, out=out[s],
+                                           workspace=ws_g)
+
+    grow_us = {}
+    for name, fn in (("append", append_all), ("append+step", grow_all)):
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(args.steps):
+            g.replay()
+        a1.record()
+        torch.cuda.synchronize()
+        grow_us[name] = a0.elapsed_time(a1) * 1e3 / (args.steps * nsteps)
+    app_bytes = 8 * B * Hkv * D * w.elem_bytes  # read k_new, v_new; write K, V; min, max RMW
+    growing = dict(capacity=cap, appends=nsteps, append_us=round(grow_us["append"], 3),
+                   append_bytes=app_bytes, append_plus_step_us=round(grow_us["append+step"], 3),
+                   step_topk=tk_g, sync_status=rkv.decode_workspace_status(ws_g))
+
     per_topk = {}
     stages_out = {}
     split_us = {name: ms * 1e3 / nsteps for name, ms in stage_ms.items() if name.startswith("split_")}
@@ -367,7 +414,8 @@ def main() -> int:
                     context=w.L, window=w.W, pool_kernel=w.pool_kernel, keep=w.keep,
                     page_size=w.page_size, channels=w.r, topk=list(w.topk),
                     decode_steps=nsteps, replicas=R),
-        per_topk=per_topk, stages=stages, roofline=roofline, sync_status=status,
+        per_topk=per_topk, stages=stages, growing_cache=growing, roofline=roofline,
+        sync_status=status,
         wall_ms_timed=round(wall_ms, 1))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_steps)

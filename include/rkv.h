@@ -198,6 +198,44 @@ int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t
                            int32_t* chan_idx, float* page_scores, int32_t* page_idx, void* out,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Decode-time append into a compressed cache that grows ([rebuttal] "SCBench Results": plain
+ * SnapKV compresses only the prompt's KV, so generated tokens join the cache as decoding goes
+ * on; "Explanation of Calculating Approximate Attention Scores": each page of consecutive
+ * tokens keeps its element-wise minimum and maximum). The caches and summaries are laid out for
+ * a fixed capacity of cap token slots per (b, h), of which the first Lc are valid:
+ *
+ * k_c, v_c       [B, Hkv, cap, D]           compressed keys and values
+ * kmin_t, kmax_t [B, Hkv, D, Pcap]          channel-major summaries, Pcap = ceil(cap/page_size);
+ *                                           page p holds the summary of slots [p*page_size,
+ *                                           min((p+1)*page_size, Lc)) for p < ceil(Lc/page_size)
+ *
+ * rkv_build_page_summaries_cap: rkv_build_page_summaries over the first Lc slots of a cache of
+ *   capacity cap (1 <= Lc <= cap); pages from ceil(Lc/page_size) on are not written.
+ * rkv_kv_append: k_new, v_new [B, Hkv, D] go to slot Lc (0 <= Lc < cap), and k_new folds into
+ *   page Lc/page_size: a slot at a page boundary starts the page (min = max = k_new), any other
+ *   replaces the page's min (max) where k_new is strictly smaller (larger). The result is
+ *   bit-identical to rkv_build_page_summaries_cap over Lc + 1 slots. The caller then uses Lc + 1.
+ * rkv_hybrid_decode_step_cap: rkv_hybrid_decode_step over the first Lc slots (P =
+ *   ceil(Lc/page_size) pages) of caches and summaries of capacity cap. Size its workspace with
+ *   rkv_hybrid_decode_workspace_bytes(B, Hq, Hkv, cap, ...): the workspace is laid out for the
+ *   capacity, so one workspace serves every Lc <= cap of that capacity (initialised once).
+ * Requires the limits of the calls they extend, Pcap <= 8192 for the step, pointers to
+ * 16-byte-aligned memory. Errors as everywhere: nothing is written when a call returns nonzero.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_build_page_summaries_cap(const void* k_c, int B, int Hkv, int Lc, int cap, int D,
+                                 int page_size, int dtype, void* kmin_t, void* kmax_t,
+                                 void* stream);
+int rkv_kv_append(const void* k_new, const void* v_new, int B, int Hkv, int Lc, int cap, int D,
+                  int page_size, int dtype, void* k_c, void* v_c, void* kmin_t, void* kmax_t,
+                  void* stream);
+int rkv_hybrid_decode_step_cap(const void* q, const void* kmin_t, const void* kmax_t,
+                               const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
+                               int cap, int D, int page_size, int r, int n_pages, float scale,
+                               int dtype, int32_t* chan_idx, float* page_scores,
+                               int32_t* page_idx, void* out, void* ws, size_t ws_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ Readings where the pages are silent (each listed with its reason in the design n
   same-size box over the prefix (average by default, max optional), applied after the group sum;
   `keep` counts the W window tokens, which are always kept; kept tokens stay in ascending
   position order; query head g belongs to KV head g // G; pages are ps consecutive slots of the
-  compressed cache and a partial last page covers only its valid slots; channels are chosen from
+  compressed cache and a partial last page covers only its valid slots (a token appended during
+  decoding extends the last page, or starts a new one at a page boundary); channels are chosen from
   sum_g |q_g| and the bound uses qbar = sum_g q_g; k tokens mean k/ps whole pages.
 
 Parity pins: every function here is pinned by tests/test_oracle_pins.py against closed forms,
@@ -171,6 +172,31 @@ def page_summaries(k_c_head: np.ndarray, page_size: int):
         kmin[:, p] = page.min(axis=0)
         kmax[:, p] = page.max(axis=0)
     return kmin, kmax
+
+
+def kv_append(k_c_head: np.ndarray, v_c_head: np.ndarray, kmin_t: np.ndarray,
+               kmax_t: np.ndarray, Lc: int, k_new: np.ndarray, v_new: np.ndarray,
+               page_size: int):
+    """Decode-time append of one token to a compressed cache that grows (rebuttal, "SCBench
+    Results": plain SnapKV compresses only the prompt, generated tokens join the cache; the page
+    summaries of "Explanation of Calculating Approximate Attention Scores").
+
+    k_c_head, v_c_head [cap, D] hold Lc valid slots; kmin_t, kmax_t [D, ceil(cap/ps)] summarise
+    the first ceil(Lc/ps) pages. Slot Lc takes (k_new, v_new), and the summary of page
+    Lc // page_size is recomputed from that page's slots up to and including Lc. Returns new
+    arrays (the inputs are not modified).
+    """
+    k = np.array(k_c_head, dtype=np.float64)
+    v = np.array(v_c_head, dtype=np.float64)
+    kmin = np.array(kmin_t, dtype=np.float64)
+    kmax = np.array(kmax_t, dtype=np.float64)
+    k[Lc] = k_new
+    v[Lc] = v_new
+    p = Lc // page_size
+    page = k[p * page_size:Lc + 1]
+    kmin[:, p] = page.min(axis=0)
+    kmax[:, p] = page.max(axis=0)
+    return k, v, kmin, kmax
 
 
 def select_channels(q_grp: np.ndarray, r: int):

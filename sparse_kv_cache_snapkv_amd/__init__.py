@@ -11,6 +11,9 @@ from .api import (  # noqa: F401
     rkv_hybrid_decode_workspace,
     rkv_hybrid_decode_step,
     rkv_build_page_summaries,
+    rkv_build_page_summaries_cap,
+    rkv_kv_append,
+    rkv_hybrid_decode_step_cap,
     rkv_hybrid_approx_scores,
     rkv_snapkvpp_evict,
     rkv_sparse_attend_decode,

@@ -217,7 +217,7 @@ def rkv_hybrid_decode_step(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.
                            page_idx: Optional[torch.Tensor] = None,
                            out: Optional[torch.Tensor] = None,
                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Fused decode step (two launches). q [B,Hq,D]; summaries [B,Hkv,D,P]; k_c, v_c
+    """Fused decode step (one launch). q [B,Hq,D]; summaries [B,Hkv,D,P]; k_c, v_c
     [B,Hkv,Lc,D] -> out [B,Hq,D]. Optional outputs: chan_idx, page_scores, page_idx."""
     B, Hq, D = q.shape
     Hkv, Lc = k_c.shape[1], k_c.shape[2]
@@ -233,6 +233,80 @@ def rkv_hybrid_decode_step(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.
         _dev(q, "q"), _dev(kmin_t, "kmin_t", q.dtype), _dev(kmax_t, "kmax_t", q.dtype),
         _dev(k_c, "k_c", q.dtype), _dev(v_c, "v_c", q.dtype), B, Hq, Hkv, Lc, D, page_size, r,
         n_pages, scale, dt, opt(chan_idx, "chan_idx", torch.int32),
+        opt(page_scores, "page_scores", torch.float32), opt(page_idx, "page_idx", torch.int32),
+        _dev(out, "out", q.dtype), ws, wsb, _stream(q)))
+    return out
+
+
+# ----------------------------------------------------------------------------- growing caches
+def _cap_shapes(k_c: torch.Tensor, kmin_t: torch.Tensor, page_size: int) -> Tuple[int, int]:
+    cap = k_c.shape[2]
+    pcap = -(-cap // page_size)
+    if kmin_t.shape[-1] != pcap:
+        raise ValueError(f"summaries must have ceil(cap/page_size) = {pcap} pages per row "
+                         f"(got {kmin_t.shape[-1]})")
+    return cap, pcap
+
+
+def rkv_build_page_summaries_cap(k_c: torch.Tensor, Lc: int, page_size: int, *,
+                                 kmin_t: Optional[torch.Tensor] = None,
+                                 kmax_t: Optional[torch.Tensor] = None):
+    """k_c [B,Hkv,cap,D] (first Lc slots valid) -> (kmin_t, kmax_t) [B,Hkv,D,ceil(cap/ps)]."""
+    B, Hkv, cap, D = k_c.shape
+    pcap = -(-cap // page_size)
+    if kmin_t is None:
+        kmin_t = torch.empty((B, Hkv, D, pcap), dtype=k_c.dtype, device=k_c.device)
+    if kmax_t is None:
+        kmax_t = torch.empty((B, Hkv, D, pcap), dtype=k_c.dtype, device=k_c.device)
+    _cap_shapes(k_c, kmin_t, page_size)
+    _check("rkv_build_page_summaries_cap", _lib.load().rkv_build_page_summaries_cap(
+        _dev(k_c, "k_c"), B, Hkv, Lc, cap, D, page_size, _dtype_code(k_c),
+        _dev(kmin_t, "kmin_t", k_c.dtype), _dev(kmax_t, "kmax_t", k_c.dtype), _stream(k_c)))
+    return kmin_t, kmax_t
+
+
+def rkv_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tensor,
+                  kmin_t: torch.Tensor, kmax_t: torch.Tensor, Lc: int, page_size: int) -> int:
+    """Writes k_new, v_new [B,Hkv,D] to slot Lc of k_c, v_c [B,Hkv,cap,D] and folds k_new into
+    its page summary (kmin_t, kmax_t [B,Hkv,D,ceil(cap/ps)]). Returns the new length Lc + 1."""
+    B, Hkv, cap, D = k_c.shape
+    _cap_shapes(k_c, kmin_t, page_size)
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new, v_new must be [B, Hkv, D] of the caches")
+    dt = k_c.dtype
+    _check("rkv_kv_append", _lib.load().rkv_kv_append(
+        _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt), B, Hkv, Lc, cap, D, page_size,
+        _dtype_code(k_c), _dev(k_c, "k_c"), _dev(v_c, "v_c", dt), _dev(kmin_t, "kmin_t", dt),
+        _dev(kmax_t, "kmax_t", dt), _stream(k_c)))
+    return Lc + 1
+
+
+def rkv_hybrid_decode_step_cap(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.Tensor,
+                               k_c: torch.Tensor, v_c: torch.Tensor, Lc: int, page_size: int,
+                               r: int, n_pages: int, scale: Optional[float] = None, *,
+                               chan_idx: Optional[torch.Tensor] = None,
+                               page_scores: Optional[torch.Tensor] = None,
+                               page_idx: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """rkv_hybrid_decode_step over the first Lc slots of caches of capacity cap = k_c.shape[2]
+    (summaries [B,Hkv,D,ceil(cap/ps)]); the workspace is rkv_hybrid_decode_workspace(q, Hkv,
+    cap, page_size, n_pages)."""
+    B, Hq, D = q.shape
+    Hkv = k_c.shape[1]
+    cap, _ = _cap_shapes(k_c, kmin_t, page_size)
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = rkv_hybrid_decode_workspace(q, Hkv, cap, page_size, n_pages)
+    ws, wsb = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    opt = lambda t, n, d: _dev(t, n, d) if t is not None else None  # noqa: E731
+    _check("rkv_hybrid_decode_step_cap", _lib.load().rkv_hybrid_decode_step_cap(
+        _dev(q, "q"), _dev(kmin_t, "kmin_t", q.dtype), _dev(kmax_t, "kmax_t", q.dtype),
+        _dev(k_c, "k_c", q.dtype), _dev(v_c, "v_c", q.dtype), B, Hq, Hkv, Lc, cap, D, page_size,
+        r, n_pages, scale, dt, opt(chan_idx, "chan_idx", torch.int32),
         opt(page_scores, "page_scores", torch.float32), opt(page_idx, "page_idx", torch.int32),
         _dev(out, "out", q.dtype), ws, wsb, _stream(q)))
     return out

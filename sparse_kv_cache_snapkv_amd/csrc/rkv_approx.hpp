@@ -110,12 +110,13 @@ constexpr int kScoreGroups = 16;
 constexpr int kScoreBatch = kApproxMaxD / kScoreGroups;  // every row load of a lane in flight
 
 // Thread layout: lane = 16 * vector + group. VEC: a vector is 16 bytes of consecutive pages
-// (p_begin a multiple of the vector width, P a multiple of it); otherwise one page per vector.
-// Scores pages [p_begin, p_end) of one (b, h) and hands each score to sink(page, value), called
-// by one lane per page. No barrier; the whole row of a vector must be active together.
+// (p_begin and the row pitch multiples of the vector width); otherwise one page per vector.
+// Scores pages [p_begin, p_end) of one (b, h), whose summary rows are `pitch` pages apart, and
+// hands each score to sink(page, value), called by one lane per page. No barrier; the whole row
+// of a vector must be active together.
 template <typename T, bool VEC, typename Sink>
 __device__ __forceinline__ void score_page_range(const T* __restrict__ kmin_bh,
-                                                 const T* __restrict__ kmax_bh, int D, int P,
+                                                 const T* __restrict__ kmax_bh, int D, int pitch,
                                                  int r, int p_begin, int p_end,
                                                  const ChannelShared& ch, Sink&& sink) {
   constexpr int V = VEC ? vec16<T>::n : 1;
@@ -140,7 +141,7 @@ __device__ __forceinline__ void score_page_range(const T* __restrict__ kmin_bh,
         const int j = grp + (u < nj ? u : 0) * kScoreGroups;
         qcv[u] = u < nj ? ch.qc[j] : 0.f;
         const int c = min(max(ch.chan[j], 0), D - 1);
-        rows[u] = (qcv[u] >= 0.f ? kmax_bh : kmin_bh) + (size_t)c * P + p;
+        rows[u] = (qcv[u] >= 0.f ? kmax_bh : kmin_bh) + (size_t)c * pitch + p;
       }
       if constexpr (VEC) {
         uint4 raw[kScoreBatch];

@@ -344,6 +344,8 @@ struct StepArgs {
   const void* k_c;
   const void* v_c;
   int BH, Hkv, Lc, ps, n_pages, P, r, pps, ppb1, nsplit, nsplit_att, part_cap, vec;
+  int kv_pitch;  // token slots per head of k_c, v_c (>= Lc)
+  int s_pitch;   // pages per channel row of the summaries (>= P)
   float scale2;
   int32_t* chan_idx;     // optional [BH, r]
   float* page_scores;    // optional [BH, P]
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
     for (int j = tid; j < a.r; j += kStepThreads) a.chan_idx[(size_t)bh * a.r + j] = ch.chan[j];
   {
     const int pb_lo = split * a.ppb1, pb_hi = min(a.P, pb_lo + a.ppb1);
-    const size_t sbase = (size_t)bh * D * a.P;
+    const size_t sbase = (size_t)bh * D * a.s_pitch;
     const T* kmin_bh = static_cast<const T*>(a.kmin_t) + sbase;
     const T* kmax_bh = static_cast<const T*>(a.kmax_t) + sbase;
     float* pso = a.page_scores != nullptr ? a.page_scores + (size_t)bh * a.P : nullptr;
@@ -469,9 +471,9 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
       if (pso != nullptr) pso[p] = v;
     };
     if (a.vec)
-      score_page_range<T, true>(kmin_bh, kmax_bh, D, a.P, a.r, pb_lo, pb_hi, ch, sink);
+      score_page_range<T, true>(kmin_bh, kmax_bh, D, a.s_pitch, a.r, pb_lo, pb_hi, ch, sink);
     else
-      score_page_range<T, false>(kmin_bh, kmax_bh, D, a.P, a.r, pb_lo, pb_hi, ch, sink);
+      score_page_range<T, false>(kmin_bh, kmax_bh, D, a.s_pitch, a.r, pb_lo, pb_hi, ch, sink);
   }
   if (!attends) return;  // a scoring-only block
 
@@ -497,8 +499,8 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
   }
   const int p_lo = split * a.pps;
   const int p_hi = min(p_lo + a.pps, a.n_pages);
-  const T* kc_bh = static_cast<const T*>(a.k_c) + (size_t)bh * a.Lc * D;
-  const T* vc_bh = static_cast<const T*>(a.v_c) + (size_t)bh * a.Lc * D;
+  const T* kc_bh = static_cast<const T*>(a.k_c) + (size_t)bh * a.kv_pitch * D;
+  const T* vc_bh = static_cast<const T*>(a.v_c) + (size_t)bh * a.kv_pitch * D;
   int32_t* pout = (a.page_idx != nullptr && split == 0) ? a.page_idx + (size_t)bh * a.n_pages
                                                         : nullptr;
   if (a.n_pages >= a.P) {
@@ -820,12 +822,14 @@ hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream) {
 
 hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
                               const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
-                              int D, int page_size, int r, int n_pages, float scale, int dtype,
-                              int32_t* chan_idx, float* page_scores, int32_t* page_idx, void* out,
-                              void* ws, hipStream_t stream) {
+                              int cap, int D, int page_size, int r, int n_pages, float scale,
+                              int dtype, int32_t* chan_idx, float* page_scores, int32_t* page_idx,
+                              void* out, void* ws, hipStream_t stream) {
   const int BH = B * Hkv;
   const int P = (Lc + page_size - 1) / page_size;
-  const StepLayout lo = step_layout(B, Hq, Hkv, D, P);
+  const int Pcap = (cap + page_size - 1) / page_size;
+  // laid out for the capacity, so a growing cache never moves a head's exchanged words
+  const StepLayout lo = step_layout(B, Hq, Hkv, D, Pcap);
   StepPlan pl = plan_step_any(dtype, D, BH, page_size, n_pages, device_cus());
   if (pl.nsplit > lo.part_cap) return hipErrorInvalidValue;  // cannot happen: cap is the maximum
   char* w = static_cast<char*>(ws);
@@ -833,7 +837,8 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   int ppb1 = (P + pl.nsplit - 1) / pl.nsplit;
   ppb1 = (ppb1 + vmax - 1) / vmax * vmax;
   StepArgs a{q, kmin_t, kmax_t, k_c, v_c, BH, Hkv, Lc, page_size, n_pages, P, r, pl.pps, ppb1,
-             pl.nsplit, pl.nsplit_att, lo.part_cap, P % vmax == 0, scale * kLog2e, chan_idx,
+             pl.nsplit, pl.nsplit_att, lo.part_cap, Pcap % vmax == 0, cap, Pcap,
+             scale * kLog2e, chan_idx,
              page_scores, page_idx, reinterpret_cast<uint64_t*>(w + lo.off_xscores),
              reinterpret_cast<uint64_t*>(w + lo.off_xpart),
              reinterpret_cast<unsigned*>(w + lo.off_sync), out};

@@ -7,9 +7,15 @@
 
 namespace rkv {
 
-// Element-wise page min/max of k_c [BH, Lc, D] into channel-major [BH, D, P].
-hipError_t launch_page_minmax(const void* k_c, int BH, int Lc, int D, int page_size, int dtype,
-                              void* kmin_t, void* kmax_t, hipStream_t stream);
+// Element-wise page min/max of the first Lc slots of k_c [BH, cap, D] into channel-major
+// [BH, D, ceil(cap/page_size)] (its first ceil(Lc/page_size) pages).
+hipError_t launch_page_minmax(const void* k_c, int BH, int Lc, int cap, int D, int page_size,
+                              int dtype, void* kmin_t, void* kmax_t, hipStream_t stream);
+
+// One token per (b, h) into slot Lc of caches of capacity cap, folded into its page summary.
+hipError_t launch_kv_append(const void* k_new, const void* v_new, int BH, int Lc, int cap, int D,
+                            int page_size, int dtype, void* k_c, void* v_c, void* kmin_t,
+                            void* kmax_t, hipStream_t stream);
 
 // Channel selection and sign-selected page bounds.
 hipError_t launch_approx_scores(const void* q, const void* kmin_t, const void* kmax_t, int B,
@@ -33,11 +39,13 @@ hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int n_pages,
                        int dtype);
 hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream);
+// Caches of capacity cap slots per head (the first Lc valid), summaries of ceil(cap/page_size)
+// pages per channel row; the workspace is laid out for the capacity.
 hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
                               const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
-                              int D, int page_size, int r, int n_pages, float scale, int dtype,
-                              int32_t* chan_idx, float* page_scores, int32_t* page_idx, void* out,
-                              void* ws, hipStream_t stream);
+                              int cap, int D, int page_size, int r, int n_pages, float scale,
+                              int dtype, int32_t* chan_idx, float* page_scores, int32_t* page_idx,
+                              void* out, void* ws, hipStream_t stream);
 
 // SnapKV++ eviction.
 size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype);

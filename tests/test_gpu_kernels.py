@@ -445,3 +445,102 @@ def test_fused_decode_step_graph_replays(rkv):
         assert torch.equal(out, eager[s][0]), f"replay {rep} output"
         assert torch.equal(pages, eager[s][1]), f"replay {rep} pages"
     assert rkv.decode_workspace_status(ws) == 0
+
+
+# ----------------------------------------------------------------------------- growing cache
+
+def _randn(shape, g, dt):
+    return torch.randn(shape, device="cuda", generator=g).to(dt)
+
+
+@pytest.mark.parametrize("dtype,D,ps", [("bf16", 128, 4), ("fp32", 64, 3), ("bf16", 64, 1)])
+def test_kv_append_bit_exact(rkv, dtype, D, ps):
+    # tokens appended one at a time into caches of fixed capacity: rows and page summaries equal
+    # the oracle's append chain, and the batch summaries of the grown cache, bit for bit
+    B, Hkv, cap, L0, n = 2, 3, 61, 17, 30
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(21)
+    k_all, v_all = _randn((B, Hkv, L0 + n, D), g, dt), _randn((B, Hkv, L0 + n, D), g, dt)
+    k_c = torch.zeros((B, Hkv, cap, D), dtype=dt, device="cuda")
+    v_c = torch.zeros_like(k_c)
+    k_c[:, :, :L0] = k_all[:, :, :L0]
+    v_c[:, :, :L0] = v_all[:, :, :L0]
+    kmin, kmax = rkv.rkv_build_page_summaries_cap(k_c, L0, ps)
+    pcap = -(-cap // ps)
+    assert kmin.shape == (B, Hkv, D, pcap)
+    ka, va = O.widen(H(k_all)), O.widen(H(v_all))
+    ref = {}
+    for b in range(B):
+        for h in range(Hkv):
+            kk = np.zeros((cap, D))
+            vv = np.zeros((cap, D))
+            kk[:L0], vv[:L0] = ka[b, h, :L0], va[b, h, :L0]
+            mn, mx = np.zeros((D, pcap)), np.zeros((D, pcap))
+            p0 = -(-L0 // ps)
+            mn[:, :p0], mx[:, :p0] = O.page_summaries(ka[b, h, :L0], ps)
+            ref[b, h] = [kk, vv, mn, mx]
+    Lc = L0
+    for _ in range(n):
+        for (b, h), st in ref.items():
+            ref[b, h] = list(O.kv_append(*st, Lc, ka[b, h, Lc], va[b, h, Lc], ps))
+        Lc = rkv.rkv_kv_append(k_all[:, :, Lc].contiguous(), v_all[:, :, Lc].contiguous(), k_c, v_c,
+                               kmin, kmax, Lc, ps)
+    torch.cuda.synchronize()
+    P = -(-Lc // ps)
+    gk, gv = O.widen(H(k_c)), O.widen(H(v_c))
+    gmin, gmax = O.widen(H(kmin[..., :P])), O.widen(H(kmax[..., :P]))  # pages past P unwritten
+    for (b, h), (kk, vv, mn, mx) in ref.items():
+        assert np.array_equal(gk[b, h, :Lc], kk[:Lc]) and np.array_equal(gv[b, h, :Lc], vv[:Lc])
+        assert np.array_equal(gmin[b, h], mn[:, :P]), f"kmin b{b} h{h}"
+        assert np.array_equal(gmax[b, h], mx[:, :P]), f"kmax b{b} h{h}"
+    bmin, bmax = rkv.rkv_build_page_summaries_cap(k_c, Lc, ps)
+    torch.cuda.synchronize()
+    assert torch.equal(bmin[..., :P].view(torch.int16 if dtype == "bf16" else torch.int32),
+                       kmin[..., :P].view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.equal(bmax[..., :P].view(torch.int16 if dtype == "bf16" else torch.int32),
+                       kmax[..., :P].view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+@pytest.mark.parametrize("cap", [1104, 1152], ids=["pitch-not-vector-multiple", "pitch-vector-multiple"])
+def test_decode_step_cap_on_growing_cache(rkv, cap):
+    # decode steps between appends on caches laid out for a capacity, one workspace for every
+    # length: channels, scores and pages equal the three calls on a dense copy, outputs the oracle
+    B, Hq, Hkv, D, ps, r, L0 = 1, 8, 2, 128, 4, 32, 1001
+    dt = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(23)
+    k_c = _randn((B, Hkv, cap, D), g, dt)
+    v_c = _randn((B, Hkv, cap, D), g, dt)
+    kmin, kmax = rkv.rkv_build_page_summaries_cap(k_c, L0, ps)
+    Lc = L0
+    for n_pages in (16, 64):
+        q0 = _randn((B, Hq, D), g, dt)
+        ws = rkv.rkv_hybrid_decode_workspace(q0, Hkv, cap, ps, n_pages)
+        for step in range(3):
+            for _ in range(7):
+                Lc = rkv.rkv_kv_append(_randn((B, Hkv, D), g, dt), _randn((B, Hkv, D), g, dt), k_c,
+                                       v_c, kmin, kmax, Lc, ps)
+            q = _randn((B, Hq, D), g, dt)
+            P = -(-Lc // ps)
+            chans = torch.empty((B, Hkv, r), dtype=torch.int32, device="cuda")
+            scores = torch.empty((B, Hkv, P), dtype=torch.float32, device="cuda")
+            pages = torch.empty((B, Hkv, n_pages), dtype=torch.int32, device="cuda")
+            out = rkv.rkv_hybrid_decode_step_cap(q, kmin, kmax, k_c, v_c, Lc, ps, r, n_pages,
+                                                 chan_idx=chans, page_scores=scores,
+                                                 page_idx=pages, workspace=ws)
+            kd, vd = k_c[:, :, :Lc].contiguous(), v_c[:, :, :Lc].contiguous()
+            dmin, dmax = rkv.rkv_build_page_summaries(kd, ps)
+            s2, c2 = rkv.rkv_hybrid_approx_scores(q, dmin, dmax, r, return_channels=True)
+            p2 = rkv.rkv_topk_select(s2, n_pages)
+            torch.cuda.synchronize()
+            assert rkv.decode_workspace_status(ws) == 0
+            assert torch.equal(chans, c2)
+            assert torch.equal(scores.view(torch.int32), s2.view(torch.int32)), "scores differ"
+            assert torch.equal(pages, p2), f"pages differ at Lc={Lc}"
+            got, pg, q64 = O.widen(H(out)), pages.cpu().numpy(), O.widen(H(q))
+            G = Hq // Hkv
+            for h in range(Hkv):
+                toks = O.page_tokens(pg[0, h], ps, Lc)
+                ref = O.sparse_attention(q64[0, h * G:(h + 1) * G], O.widen(H(kd[0, h])),
+                                         O.widen(H(vd[0, h])), toks, 1 / math.sqrt(D))
+                assert_rows_close(got[0, h * G:(h + 1) * G], ref, TOL_OUT["bf16"],
+                                  f"Lc={Lc} n_pages={n_pages} h{h}")

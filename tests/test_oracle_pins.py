@@ -225,6 +225,41 @@ def test_page_summaries_bounds_attained_partial_page():
     assert np.array_equal(k1min, k.T) and np.array_equal(k1max, k.T)
 
 
+@pytest.mark.parametrize("ps", [1, 3, 4])
+def test_kv_append_grows_pages_by_brute_force(ps):
+    # appending one slot at a time from an empty cache: every written page's (min, max) bounds
+    # each of its valid rows and is attained by one of them (brute force), pages are started at
+    # page boundaries, unwritten slots and pages stay untouched, and the end state is the batch
+    # summary of the grown cache
+    rng = np.random.default_rng(30 + ps)
+    cap, D, n = 14, 5, 11
+    k_all = rng.standard_normal((n, D))
+    v_all = rng.standard_normal((n, D))
+    pcap = -(-cap // ps)
+    k = np.full((cap, D), 7.0)
+    v = np.full((cap, D), 7.0)
+    kmin = np.full((D, pcap), 9.0)
+    kmax = np.full((D, pcap), 9.0)
+    for Lc in range(n):
+        k, v, kmin, kmax = O.kv_append(k, v, kmin, kmax, Lc, k_all[Lc], v_all[Lc], ps)
+        L1 = Lc + 1
+        assert np.array_equal(k[:L1], k_all[:L1]) and np.array_equal(v[:L1], v_all[:L1])
+        assert np.all(k[L1:] == 7.0) and np.all(v[L1:] == 7.0)
+        np_ = -(-L1 // ps)
+        for p in range(np_):
+            rows = k_all[p * ps:min(p * ps + ps, L1)]
+            assert np.all(kmin[:, p] <= rows.min(axis=0)) and np.all(rows.max(axis=0) <= kmax[:, p])
+            for c in range(D):
+                assert kmin[c, p] in rows[:, c] and kmax[c, p] in rows[:, c]
+        assert np.all(kmin[:, np_:] == 9.0) and np.all(kmax[:, np_:] == 9.0)
+        if Lc % ps == 0:  # a page boundary: the new page is the row itself
+            assert np.array_equal(kmin[:, Lc // ps], k_all[Lc])
+            assert np.array_equal(kmax[:, Lc // ps], k_all[Lc])
+    bmin, bmax = O.page_summaries(k_all, ps)
+    assert np.array_equal(kmin[:, :bmin.shape[1]], bmin)
+    assert np.array_equal(kmax[:, :bmax.shape[1]], bmax)
+
+
 def test_bound_is_box_maximum_by_vertex_enumeration():
     rng = np.random.default_rng(8)
     D, P, r = 7, 9, 4
