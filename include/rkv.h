@@ -236,6 +236,32 @@ int rkv_hybrid_decode_step_cap(const void* q, const void* kmin_t, const void* km
                                int32_t* page_idx, void* out, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * RocketKV-MT, the multi-turn variant ([rebuttal] "SCBench Results": SnapKV++ does not evict
+ * permanently; every prompt token stays in memory, and each decode step selects only among the
+ * tokens SnapKV++ kept). The compressed cache is a view: slot t of (b, h) is row
+ * kept_idx[b,h,t] of the full cache.
+ *
+ * k, v      [B, Hkv, L, D]   the full caches
+ * kept_idx  [B, Hkv, Lc]     int32 rows of the view, e.g. rkv_snapkvpp_evict's kept_idx with
+ *                            k_out = v_out = NULL; values outside [0, L) are clamped into it
+ * rkv_build_page_summaries_indexed: rkv_build_page_summaries of the view (kmin_t, kmax_t
+ *   [B, Hkv, D, ceil(Lc/page_size)]); bit-identical to summarising the gathered rows.
+ * rkv_hybrid_decode_step_indexed: rkv_hybrid_decode_step over the view; its workspace is
+ *   rkv_hybrid_decode_workspace_bytes(B, Hq, Hkv, Lc, ...). Channels, scores, pages and outputs
+ *   are bit-identical to rkv_hybrid_decode_step on the gathered caches.
+ * Requires the limits of the calls they extend.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_build_page_summaries_indexed(const void* k, const int32_t* kept_idx, int B, int Hkv,
+                                     int L, int Lc, int D, int page_size, int dtype, void* kmin_t,
+                                     void* kmax_t, void* stream);
+int rkv_hybrid_decode_step_indexed(const void* q, const void* kmin_t, const void* kmax_t,
+                                   const void* k, const void* v, const int32_t* kept_idx, int B,
+                                   int Hq, int Hkv, int L, int Lc, int D, int page_size, int r,
+                                   int n_pages, float scale, int dtype, int32_t* chan_idx,
+                                   float* page_scores, int32_t* page_idx, void* out, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

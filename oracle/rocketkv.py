@@ -277,6 +277,19 @@ def hybrid_decode_step(q, k_c, v_c, kmin_t, kmax_t, page_size: int, r: int, topk
     return dict(chans=chans, scores=scores, pages=pages, out=out)
 
 
+def mt_view(k, v, kept):
+    """RocketKV-MT (rebuttal, "SCBench Results"): SnapKV++ keeps every prompt token in memory and
+    decoding selects only among the tokens it kept. The compressed cache is the view whose slot t
+    of (b, h) is row kept[b, h, t] of the full caches k, v [B,Hkv,L,D]; the hybrid step then runs
+    on that view unchanged. Returns the gathered (k_c, v_c) [B,Hkv,Lc,D] in float64."""
+    k, v = widen(k), widen(v)
+    kept = np.asarray(kept, dtype=np.int64)
+    B, Hkv = kept.shape[:2]
+    k_c = np.stack([np.stack([k[b, h, kept[b, h]] for h in range(Hkv)]) for b in range(B)])
+    v_c = np.stack([np.stack([v[b, h, kept[b, h]] for h in range(Hkv)]) for b in range(B)])
+    return k_c, v_c
+
+
 def summaries(k_c, page_size: int):
     """page_summaries over a batch: k_c [B,Hkv,Lc,D] -> (kmin_t, kmax_t) [B,Hkv,D,P]."""
     k_c = widen(k_c)

@@ -32,6 +32,9 @@ SIGNATURES = {
     "rkv_kv_append": (_c_int, [_vp, _vp] + [_c_int] * 7 + [_vp, _vp, _vp, _vp, _vp]),
     "rkv_hybrid_decode_step_cap": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int]
                                    + [_vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "rkv_build_page_summaries_indexed": (_c_int, [_vp, _vp] + [_c_int] * 7 + [_vp, _vp, _vp]),
+    "rkv_hybrid_decode_step_indexed": (_c_int, [_vp] * 6 + [_c_int] * 9 + [_c_float, _c_int]
+                                       + [_vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 _lib = None

@@ -312,6 +312,64 @@ def rkv_hybrid_decode_step_cap(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: to
     return out
 
 
+# ----------------------------------------------------------------------------- multi-turn variant
+def _kept_rows(k: torch.Tensor, kept_idx: torch.Tensor) -> int:
+    B, Hkv, L, D = k.shape
+    if kept_idx.dim() != 3 or tuple(kept_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("kept_idx must be [B, Hkv, Lc] of the cache")
+    _dev(kept_idx, "kept_idx", torch.int32)
+    return kept_idx.shape[2]
+
+
+def rkv_build_page_summaries_indexed(k: torch.Tensor, kept_idx: torch.Tensor, page_size: int, *,
+                                     kmin_t: Optional[torch.Tensor] = None,
+                                     kmax_t: Optional[torch.Tensor] = None):
+    """Summaries of the view k[b, h, kept_idx[b, h]] of the full cache k [B,Hkv,L,D]:
+    (kmin_t, kmax_t) [B,Hkv,D,ceil(Lc/ps)]."""
+    B, Hkv, L, D = k.shape
+    Lc = _kept_rows(k, kept_idx)
+    P = -(-Lc // page_size)
+    if kmin_t is None:
+        kmin_t = torch.empty((B, Hkv, D, P), dtype=k.dtype, device=k.device)
+    if kmax_t is None:
+        kmax_t = torch.empty((B, Hkv, D, P), dtype=k.dtype, device=k.device)
+    _check("rkv_build_page_summaries_indexed", _lib.load().rkv_build_page_summaries_indexed(
+        _dev(k, "k"), kept_idx.data_ptr(), B, Hkv, L, Lc, D, page_size, _dtype_code(k),
+        _dev(kmin_t, "kmin_t", k.dtype), _dev(kmax_t, "kmax_t", k.dtype), _stream(k)))
+    return kmin_t, kmax_t
+
+
+def rkv_hybrid_decode_step_indexed(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.Tensor,
+                                   k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor,
+                                   page_size: int, r: int, n_pages: int,
+                                   scale: Optional[float] = None, *,
+                                   chan_idx: Optional[torch.Tensor] = None,
+                                   page_scores: Optional[torch.Tensor] = None,
+                                   page_idx: Optional[torch.Tensor] = None,
+                                   out: Optional[torch.Tensor] = None,
+                                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """rkv_hybrid_decode_step over the view k[b, h, kept_idx[b, h]] (and v) of the full caches
+    k, v [B,Hkv,L,D]; summaries from rkv_build_page_summaries_indexed."""
+    B, Hq, D = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    Lc = _kept_rows(k, kept_idx)
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = rkv_hybrid_decode_workspace(q, Hkv, Lc, page_size, n_pages)
+    ws, wsb = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    opt = lambda t, n, d: _dev(t, n, d) if t is not None else None  # noqa: E731
+    _check("rkv_hybrid_decode_step_indexed", _lib.load().rkv_hybrid_decode_step_indexed(
+        _dev(q, "q"), _dev(kmin_t, "kmin_t", q.dtype), _dev(kmax_t, "kmax_t", q.dtype),
+        _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), kept_idx.data_ptr(), B, Hq, Hkv, L, Lc, D,
+        page_size, r, n_pages, scale, dt, opt(chan_idx, "chan_idx", torch.int32),
+        opt(page_scores, "page_scores", torch.float32), opt(page_idx, "page_idx", torch.int32),
+        _dev(out, "out", q.dtype), ws, wsb, _stream(q)))
+    return out
+
+
 def hybrid_decode_step(q, k_c, v_c, kmin_t, kmax_t, page_size: int, r: int, topk: int,
                        scale: Optional[float] = None, *, scores=None, pages=None, out=None,
                        workspace=None):

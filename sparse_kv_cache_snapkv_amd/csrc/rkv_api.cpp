@@ -107,8 +107,9 @@ int rkv_build_page_summaries(const void* k_c, int B, int Hkv, int Lc, int D, int
   if (!dims_ok((long)B * Hkv, Lc, Lc, D)) return RKV_ERR_SHAPE;
   if (!head_dim_ok(D)) return RKV_ERR_UNSUPPORTED;
   if (!aligned16(k_c)) return RKV_ERR_SHAPE;
-  return launch_status(rkv::launch_page_minmax(k_c, B * Hkv, Lc, Lc, D, page_size, dtype, kmin_t,
-                                               kmax_t, static_cast<hipStream_t>(stream)));
+  return launch_status(rkv::launch_page_minmax(k_c, nullptr, B * Hkv, Lc, Lc, Lc, D, page_size,
+                                               dtype, kmin_t, kmax_t,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int rkv_build_page_summaries_cap(const void* k_c, int B, int Hkv, int Lc, int cap, int D,
@@ -120,8 +121,23 @@ int rkv_build_page_summaries_cap(const void* k_c, int B, int Hkv, int Lc, int ca
   if (!dims_ok((long)B * Hkv, cap, cap, D)) return RKV_ERR_SHAPE;
   if (!head_dim_ok(D)) return RKV_ERR_UNSUPPORTED;
   if (!aligned16(k_c)) return RKV_ERR_SHAPE;
-  return launch_status(rkv::launch_page_minmax(k_c, B * Hkv, Lc, cap, D, page_size, dtype,
-                                               kmin_t, kmax_t, static_cast<hipStream_t>(stream)));
+  return launch_status(rkv::launch_page_minmax(k_c, nullptr, B * Hkv, Lc, cap, cap, D, page_size,
+                                               dtype, kmin_t, kmax_t,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int rkv_build_page_summaries_indexed(const void* k, const int32_t* kept_idx, int B, int Hkv,
+                                     int L, int Lc, int D, int page_size, int dtype, void* kmin_t,
+                                     void* kmax_t, void* stream) {
+  if (!k || !kept_idx || !kmin_t || !kmax_t) return RKV_ERR_NULL;
+  if (!dtype_ok(dtype)) return RKV_ERR_DTYPE;
+  if (B < 1 || Hkv < 1 || L < 1 || Lc < 1 || page_size < 1 || D < 1) return RKV_ERR_SHAPE;
+  if (!dims_ok((long)B * Hkv, L, L, D) || !dims_ok((long)B * Hkv, Lc, 1, 1)) return RKV_ERR_SHAPE;
+  if (!head_dim_ok(D)) return RKV_ERR_UNSUPPORTED;
+  if (!aligned16(k)) return RKV_ERR_SHAPE;
+  return launch_status(rkv::launch_page_minmax(k, kept_idx, B * Hkv, Lc, L, Lc, D, page_size,
+                                               dtype, kmin_t, kmax_t,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int rkv_kv_append(const void* k_new, const void* v_new, int B, int Hkv, int Lc, int cap, int D,
@@ -239,9 +255,34 @@ int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t
     return RKV_ERR_SHAPE;
   const size_t need = rkv::decode_ws_bytes(B, Hq, Hkv, Lc, D, page_size, n_pages, dtype);
   if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return RKV_ERR_WORKSPACE;
-  return launch_status(rkv::launch_decode_step(q, kmin_t, kmax_t, k_c, v_c, B, Hq, Hkv, Lc, Lc,
-                                               D, page_size, r, n_pages, scale, dtype, chan_idx,
-                                               page_scores, page_idx, out, ws,
+  return launch_status(rkv::launch_decode_step(q, kmin_t, kmax_t, k_c, v_c, nullptr, B, Hq, Hkv,
+                                               Lc, Lc, Lc, D, page_size, r, n_pages, scale, dtype,
+                                               chan_idx, page_scores, page_idx, out, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int rkv_hybrid_decode_step_indexed(const void* q, const void* kmin_t, const void* kmax_t,
+                                   const void* k, const void* v, const int32_t* kept_idx, int B,
+                                   int Hq, int Hkv, int L, int Lc, int D, int page_size, int r,
+                                   int n_pages, float scale, int dtype, int32_t* chan_idx,
+                                   float* page_scores, int32_t* page_idx, void* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!q || !kmin_t || !kmax_t || !k || !v || !kept_idx || !out) return RKV_ERR_NULL;
+  if (!dtype_ok(dtype)) return RKV_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || Lc < 1 || page_size < 1 || n_pages < 1 || Hq % Hkv)
+    return RKV_ERR_SHAPE;
+  const int P = ceil_div(Lc, page_size);
+  if (n_pages > P || r < 1 || r > D || !isfinite(scale)) return RKV_ERR_SHAPE;
+  if (!dims_ok((long)B * Hkv, L, L, D) || !dims_ok((long)B * Hkv, Lc, 1, 1)) return RKV_ERR_SHAPE;
+  if (!head_dim_ok(D) || Hq / Hkv > 8 || P > kFusedMaxPages) return RKV_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kmin_t) ||
+      !aligned16(kmax_t))
+    return RKV_ERR_SHAPE;
+  const size_t need = rkv::decode_ws_bytes(B, Hq, Hkv, Lc, D, page_size, n_pages, dtype);
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return RKV_ERR_WORKSPACE;
+  return launch_status(rkv::launch_decode_step(q, kmin_t, kmax_t, k, v, kept_idx, B, Hq, Hkv, Lc,
+                                               L, Lc, D, page_size, r, n_pages, scale, dtype,
+                                               chan_idx, page_scores, page_idx, out, ws,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -266,9 +307,9 @@ int rkv_hybrid_decode_step_cap(const void* q, const void* kmin_t, const void* km
     return RKV_ERR_SHAPE;
   const size_t need = rkv::decode_ws_bytes(B, Hq, Hkv, cap, D, page_size, n_pages, dtype);
   if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return RKV_ERR_WORKSPACE;
-  return launch_status(rkv::launch_decode_step(q, kmin_t, kmax_t, k_c, v_c, B, Hq, Hkv, Lc, cap,
-                                               D, page_size, r, n_pages, scale, dtype, chan_idx,
-                                               page_scores, page_idx, out, ws,
+  return launch_status(rkv::launch_decode_step(q, kmin_t, kmax_t, k_c, v_c, nullptr, B, Hq, Hkv,
+                                               Lc, cap, cap, D, page_size, r, n_pages, scale,
+                                               dtype, chan_idx, page_scores, page_idx, out, ws,
                                                static_cast<hipStream_t>(stream)));
 }
 

@@ -101,8 +101,12 @@ struct WaveState {
   }
 
   // Tokens [0, ntok) of the page list `pages` (LDS): this wave takes chunks wave, wave+4, ...
+  // rows (may be null): slot t of the compressed view is row rows[t] of kc_bh / vc_bh, clamped
+  // into [0, row_hi] (the multi-turn variant keeps the whole cache and indexes its kept rows).
   __device__ __forceinline__ void run(const T* __restrict__ kc_bh, const T* __restrict__ vc_bh,
-                                      const int* pages, int ntok, int ps, int P, int Lc) {
+                                      const int* pages, int ntok, int ps, int P, int Lc,
+                                      const int32_t* __restrict__ rows = nullptr,
+                                      int row_hi = 0) {
     constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT, TPL = Geo<T, D, SLOTS>::TPL;
     constexpr int WTOK = Geo<T, D, SLOTS>::WTOK;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -121,6 +125,10 @@ struct WaveState {
         valid = valid && page >= 0 && page < P && t < Lc;
         ok[s] = valid;
         tok[s] = valid ? t : 0;
+      }
+      if (rows != nullptr) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) tok[s] = min(max(rows[tok[s]], 0), row_hi);
       }
       uint4 kr[SLOTS], vr[SLOTS];
 #pragma unroll
@@ -344,7 +352,8 @@ struct StepArgs {
   const void* k_c;
   const void* v_c;
   int BH, Hkv, Lc, ps, n_pages, P, r, pps, ppb1, nsplit, nsplit_att, part_cap, vec;
-  int kv_pitch;  // token slots per head of k_c, v_c (>= Lc)
+  int kv_pitch;  // token slots per head of k_c, v_c (>= Lc; the full length L with rows)
+  const int32_t* rows;  // optional [BH, Lc]: slot t of head bh is row rows[bh*Lc + t] of k_c, v_c
   int s_pitch;   // pages per channel row of the summaries (>= P)
   float scale2;
   int32_t* chan_idx;     // optional [BH, r]
@@ -501,6 +510,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
   const int p_hi = min(p_lo + a.pps, a.n_pages);
   const T* kc_bh = static_cast<const T*>(a.k_c) + (size_t)bh * a.kv_pitch * D;
   const T* vc_bh = static_cast<const T*>(a.v_c) + (size_t)bh * a.kv_pitch * D;
+  const int32_t* rows_bh = a.rows != nullptr ? a.rows + (size_t)bh * a.Lc : nullptr;
   int32_t* pout = (a.page_idx != nullptr && split == 0) ? a.page_idx + (size_t)bh * a.n_pages
                                                         : nullptr;
   if (a.n_pages >= a.P) {
@@ -510,7 +520,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
       __syncthreads();
       for (int i = tid; i < nw; i += kStepThreads) sh.pages[i] = w0 + i;
       __syncthreads();
-      st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc);
+      st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc, rows_bh, a.kv_pitch - 1);
     }
   } else {
     if (!multi) {
@@ -539,7 +549,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(StepArgs a) {
         }
       }
       __syncthreads();
-      st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc);
+      st.run(kc_bh, vc_bh, sh.pages, nw * a.ps, a.ps, a.P, a.Lc, rows_bh, a.kv_pitch - 1);
       w0 += kMaxPagesPerSplit;
     } while (w0 < p_hi);
   }
@@ -821,10 +831,11 @@ hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream) {
 }
 
 hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
-                              const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
-                              int cap, int D, int page_size, int r, int n_pages, float scale,
-                              int dtype, int32_t* chan_idx, float* page_scores, int32_t* page_idx,
-                              void* out, void* ws, hipStream_t stream) {
+                              const void* k_c, const void* v_c, const int32_t* rows, int B, int Hq,
+                              int Hkv, int Lc, int kv_pitch, int cap, int D, int page_size, int r,
+                              int n_pages, float scale, int dtype, int32_t* chan_idx,
+                              float* page_scores, int32_t* page_idx, void* out, void* ws,
+                              hipStream_t stream) {
   const int BH = B * Hkv;
   const int P = (Lc + page_size - 1) / page_size;
   const int Pcap = (cap + page_size - 1) / page_size;
@@ -837,7 +848,7 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   int ppb1 = (P + pl.nsplit - 1) / pl.nsplit;
   ppb1 = (ppb1 + vmax - 1) / vmax * vmax;
   StepArgs a{q, kmin_t, kmax_t, k_c, v_c, BH, Hkv, Lc, page_size, n_pages, P, r, pl.pps, ppb1,
-             pl.nsplit, pl.nsplit_att, lo.part_cap, Pcap % vmax == 0, cap, Pcap,
+             pl.nsplit, pl.nsplit_att, lo.part_cap, Pcap % vmax == 0, kv_pitch, rows, Pcap,
              scale * kLog2e, chan_idx,
              page_scores, page_idx, reinterpret_cast<uint64_t*>(w + lo.off_xscores),
              reinterpret_cast<uint64_t*>(w + lo.off_xpart),

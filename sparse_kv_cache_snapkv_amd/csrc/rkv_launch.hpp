@@ -7,10 +7,12 @@
 
 namespace rkv {
 
-// Element-wise page min/max of the first Lc slots of k_c [BH, cap, D] into channel-major
-// [BH, D, ceil(cap/page_size)] (its first ceil(Lc/page_size) pages).
-hipError_t launch_page_minmax(const void* k_c, int BH, int Lc, int cap, int D, int page_size,
-                              int dtype, void* kmin_t, void* kmax_t, hipStream_t stream);
+// Element-wise page min/max of the first Lc slots of k_c [BH, kv_pitch, D] into channel-major
+// [BH, D, ceil(cap/page_size)] (its first ceil(Lc/page_size) pages). rows (may be null): slot t
+// of head bh is row rows[bh*Lc + t] of k_c.
+hipError_t launch_page_minmax(const void* k_c, const int32_t* rows, int BH, int Lc, int kv_pitch,
+                              int cap, int D, int page_size, int dtype, void* kmin_t,
+                              void* kmax_t, hipStream_t stream);
 
 // One token per (b, h) into slot Lc of caches of capacity cap, folded into its page summary.
 hipError_t launch_kv_append(const void* k_new, const void* v_new, int BH, int Lc, int cap, int D,
@@ -39,13 +41,15 @@ hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int n_pages,
                        int dtype);
 hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream);
-// Caches of capacity cap slots per head (the first Lc valid), summaries of ceil(cap/page_size)
-// pages per channel row; the workspace is laid out for the capacity.
+// Caches of kv_pitch rows per head (slot t is row t, or rows[bh*Lc + t] when rows is given),
+// summaries of ceil(cap/page_size) pages per channel row (the first ceil(Lc/page_size) valid);
+// the workspace is laid out for cap.
 hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
-                              const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
-                              int cap, int D, int page_size, int r, int n_pages, float scale,
-                              int dtype, int32_t* chan_idx, float* page_scores, int32_t* page_idx,
-                              void* out, void* ws, hipStream_t stream);
+                              const void* k_c, const void* v_c, const int32_t* rows, int B, int Hq,
+                              int Hkv, int Lc, int kv_pitch, int cap, int D, int page_size, int r,
+                              int n_pages, float scale, int dtype, int32_t* chan_idx,
+                              float* page_scores, int32_t* page_idx, void* out, void* ws,
+                              hipStream_t stream);
 
 // SnapKV++ eviction.
 size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype);

@@ -15,9 +15,11 @@ constexpr int kThreads = 256;
 
 // One block: kPagesPerBlock pages of one (b, h). Reads token rows as 16-byte chunks, reduces
 // over each page's slots, transposes through LDS and writes [D][pages] rows. The cache holds
-// kv_pitch token slots per head (the first Lc valid) and a summary row s_pitch pages.
+// kv_pitch token slots per head (the first Lc valid) and a summary row s_pitch pages. rows (may
+// be null): slot t of head bh is row rows[bh*Lc + t] of the cache, clamped into [0, kv_pitch).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ k_c,
+                                                          const int32_t* __restrict__ rows,
                                                           T* __restrict__ kmin_t,
                                                           T* __restrict__ kmax_t, int Lc, int P,
                                                           int ps, int kv_pitch, int s_pitch) {
@@ -28,17 +30,19 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
   const int bh = blockIdx.y;
   const int p0 = blockIdx.x * kPagesPerBlock;
   const T* kb = k_c + (size_t)bh * kv_pitch * D;
+  const int32_t* rb = rows != nullptr ? rows + (size_t)bh * Lc : nullptr;
+  auto row = [&](int t) { return rb != nullptr ? min(max(rb[t], 0), kv_pitch - 1) : t; };
   for (int idx = threadIdx.x; idx < kPagesPerBlock * CH; idx += kThreads) {
     const int pl = idx / CH, ch = idx % CH, p = p0 + pl;
     if (p >= P) continue;
     const int t0 = p * ps, t1 = min(t0 + ps, Lc);
     float mn[V], mx[V];
-    unpack16<T>(load16(kb + (size_t)t0 * D + ch * V), mn);
+    unpack16<T>(load16(kb + (size_t)row(t0) * D + ch * V), mn);
 #pragma unroll
     for (int e = 0; e < V; ++e) mx[e] = mn[e];
     for (int t = t0 + 1; t < t1; ++t) {
       float x[V];
-      unpack16<T>(load16(kb + (size_t)t * D + ch * V), x);
+      unpack16<T>(load16(kb + (size_t)row(t) * D + ch * V), x);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         mn[e] = x[e] < mn[e] ? x[e] : mn[e];
@@ -89,13 +93,13 @@ __global__ void k_kv_append(const T* __restrict__ k_new, const T* __restrict__ v
 }
 
 template <typename T, int D>
-hipError_t launch_t(const void* k_c, int BH, int Lc, int cap, int ps, void* kmin_t, void* kmax_t,
-                    hipStream_t stream) {
+hipError_t launch_t(const void* k_c, const int32_t* rows, int BH, int Lc, int kv_pitch, int cap,
+                    int ps, void* kmin_t, void* kmax_t, hipStream_t stream) {
   const int P = (Lc + ps - 1) / ps;
   dim3 grid((P + kPagesPerBlock - 1) / kPagesPerBlock, BH);
   hipLaunchKernelGGL((k_page_minmax<T, D>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const T*>(k_c), static_cast<T*>(kmin_t),
-                     static_cast<T*>(kmax_t), Lc, P, ps, cap, (cap + ps - 1) / ps);
+                     static_cast<const T*>(k_c), rows, static_cast<T*>(kmin_t),
+                     static_cast<T*>(kmax_t), Lc, P, ps, kv_pitch, (cap + ps - 1) / ps);
   return hipGetLastError();
 }
 
@@ -111,13 +115,18 @@ hipError_t append_t(const void* k_new, const void* v_new, int BH, int Lc, int ca
 
 }  // namespace
 
-hipError_t launch_page_minmax(const void* k_c, int BH, int Lc, int cap, int D, int page_size,
-                              int dtype, void* kmin_t, void* kmax_t, hipStream_t stream) {
+hipError_t launch_page_minmax(const void* k_c, const int32_t* rows, int BH, int Lc, int kv_pitch,
+                              int cap, int D, int page_size, int dtype, void* kmin_t,
+                              void* kmax_t, hipStream_t stream) {
   if (dtype == 0)
-    return D == 64 ? launch_t<float, 64>(k_c, BH, Lc, cap, page_size, kmin_t, kmax_t, stream)
-                   : launch_t<float, 128>(k_c, BH, Lc, cap, page_size, kmin_t, kmax_t, stream);
-  return D == 64 ? launch_t<bf16_t, 64>(k_c, BH, Lc, cap, page_size, kmin_t, kmax_t, stream)
-                 : launch_t<bf16_t, 128>(k_c, BH, Lc, cap, page_size, kmin_t, kmax_t, stream);
+    return D == 64 ? launch_t<float, 64>(k_c, rows, BH, Lc, kv_pitch, cap, page_size, kmin_t,
+                                         kmax_t, stream)
+                   : launch_t<float, 128>(k_c, rows, BH, Lc, kv_pitch, cap, page_size, kmin_t,
+                                          kmax_t, stream);
+  return D == 64 ? launch_t<bf16_t, 64>(k_c, rows, BH, Lc, kv_pitch, cap, page_size, kmin_t,
+                                        kmax_t, stream)
+                 : launch_t<bf16_t, 128>(k_c, rows, BH, Lc, kv_pitch, cap, page_size, kmin_t,
+                                         kmax_t, stream);
 }
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, int BH, int Lc, int cap, int D,

@@ -544,3 +544,54 @@ def test_decode_step_cap_on_growing_cache(rkv, cap):
                                          O.widen(H(vd[0, h])), toks, 1 / math.sqrt(D))
                 assert_rows_close(got[0, h * G:(h + 1) * G], ref, TOL_OUT["bf16"],
                                   f"Lc={Lc} n_pages={n_pages} h{h}")
+
+
+# ----------------------------------------------------------------------------- multi-turn variant
+
+@pytest.mark.parametrize("dtype,D,Lc,ps", [("bf16", 128, 702, 4), ("fp32", 64, 333, 3)])
+def test_mt_indexed_step_equals_step_on_gathered_cache(rkv, dtype, D, Lc, ps):
+    # the view through kept rows of the full cache: summaries and every output of the fused step
+    # are bit-identical to those on the gathered cache, and the outputs match the oracle's view
+    B, Hq, Hkv, L, r = 2, 8, 2, 3001, 24
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(31)
+    k, v = _randn((B, Hkv, L, D), g, dt), _randn((B, Hkv, L, D), g, dt)
+    rng = np.random.default_rng(31)
+    kept_np = np.stack([np.stack([np.sort(rng.choice(L, Lc, replace=False)) for _ in range(Hkv)])
+                        for _ in range(B)]).astype(np.int32)
+    kept = torch.from_numpy(kept_np).cuda()
+    bi = torch.arange(B, device="cuda")[:, None, None]
+    hi = torch.arange(Hkv, device="cuda")[None, :, None]
+    kg, vg = k[bi, hi, kept.long()].contiguous(), v[bi, hi, kept.long()].contiguous()
+    kmin, kmax = rkv.rkv_build_page_summaries_indexed(k, kept, ps)
+    gmin, gmax = rkv.rkv_build_page_summaries(kg, ps)
+    torch.cuda.synchronize()
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(kmin.view(iv), gmin.view(iv)) and torch.equal(kmax.view(iv), gmax.view(iv))
+    P = kmin.shape[-1]
+    ka, va = O.mt_view(H(k), H(v), kept_np)
+    for topk in (ps, 64 * ps, 128 * ps, P * ps):
+        n_pages = min(topk // ps, P)
+        q = _randn((B, Hq, D), g, dt)
+        res = []
+        for fn, args in ((rkv.rkv_hybrid_decode_step_indexed, (q, kmin, kmax, k, v, kept)),
+                         (rkv.rkv_hybrid_decode_step, (q, gmin, gmax, kg, vg))):
+            chans = torch.empty((B, Hkv, r), dtype=torch.int32, device="cuda")
+            scores = torch.empty((B, Hkv, P), dtype=torch.float32, device="cuda")
+            pages = torch.empty((B, Hkv, n_pages), dtype=torch.int32, device="cuda")
+            out = fn(*args, ps, r, n_pages, chan_idx=chans, page_scores=scores, page_idx=pages)
+            res.append((chans, scores, pages, out))
+        torch.cuda.synchronize()
+        (c1, s1, p1, o1), (c2, s2, p2, o2) = res
+        assert torch.equal(c1, c2) and torch.equal(p1, p2), f"topk={topk}"
+        assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+        assert torch.equal(o1.view(iv), o2.view(iv)), f"outputs differ at topk={topk}"
+        got, pg, q64 = O.widen(H(o1)), p1.cpu().numpy(), O.widen(H(q))
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hkv):
+                toks = O.page_tokens(pg[b, h], ps, Lc)
+                ref = O.sparse_attention(q64[b, h * G:(h + 1) * G], ka[b, h], va[b, h], toks,
+                                         1 / math.sqrt(D))
+                assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT[dtype],
+                                  f"topk={topk} b{b} h{h}")

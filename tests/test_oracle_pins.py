@@ -260,6 +260,28 @@ def test_kv_append_grows_pages_by_brute_force(ps):
     assert np.array_equal(kmax[:, :bmax.shape[1]], bmax)
 
 
+def test_mt_view_identity_and_eviction_equivalence():
+    # the multi-turn view with every row kept is the full cache, and with SnapKV++'s kept rows it
+    # is exactly the cache that permanent eviction compacts (so the decode steps agree)
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, L, D, W, keep, ps = 1, 4, 2, 40, 8, 4, 16, 4
+    q_win = rng.standard_normal((B, Hq, W, D))
+    k = rng.standard_normal((B, Hkv, L, D))
+    v = rng.standard_normal((B, Hkv, L, D))
+    ident = np.broadcast_to(np.arange(L), (B, Hkv, L))
+    kc, vc = O.mt_view(k, v, ident)
+    assert np.array_equal(kc, k) and np.array_equal(vc, v)
+    ev = O.snapkvpp_evict(q_win, k, v, keep, 3, 1 / math.sqrt(D))
+    kc, vc = O.mt_view(k, v, ev["kept"])
+    assert np.array_equal(kc, ev["k_c"]) and np.array_equal(vc, ev["v_c"])
+    q = rng.standard_normal((B, Hq, D))
+    kmin, kmax = O.summaries(kc, ps)
+    a = O.hybrid_decode_step(q, kc, vc, kmin, kmax, ps, 4, 8, 0.3)
+    kmin2, kmax2 = O.summaries(ev["k_c"], ps)
+    b = O.hybrid_decode_step(q, ev["k_c"], ev["v_c"], kmin2, kmax2, ps, 4, 8, 0.3)
+    assert np.array_equal(a["pages"], b["pages"]) and np.array_equal(a["out"], b["out"])
+
+
 def test_bound_is_box_maximum_by_vertex_enumeration():
     rng = np.random.default_rng(8)
     D, P, r = 7, 9, 4
