@@ -57,6 +57,31 @@ int rkv_version(void);
 const char* rkv_status_string(int status);
 
 /* ------------------------------------------------------------------------------------------
+ * Budget planner (host only, no GPU work). The pages' rule for turning a token budget into the
+ * two stages' settings ([rebuttal] "Is Page Always Divided Into 4?": the compression ratio
+ * C = L / token_budget is split evenly between SnapKV++ and hybrid attention, and hybrid
+ * attention's share again evenly between the sequence (page size) and head (channels)
+ * dimensions; "Lack of Direct Latency Comparison": the budget counts the approximation's
+ * traffic, so with pages of ps tokens and r of D channels the approximation costs
+ * keep*r/(ps*2*D) tokens and the rest goes to sparse attention; "Potential Sensitivity to
+ * Kernel Size in SnapKV++": longer inputs take larger pooling kernels).
+ *
+ * With s = sqrt(C) per stage and d = sqrt(s) per dimension of the second stage:
+ *   keep          = round(L / s), clamped to [W, L]
+ *   page_size     = max(1, round(d))
+ *   r             = round(D / d), clamped to [1, D]
+ *   approx_tokens = ceil(keep * r / (page_size * 2 * D))
+ *   topk          = token_budget - approx_tokens, rounded down to a multiple of page_size and
+ *                   clamped to [page_size, keep rounded up to a page]
+ *   pool_kernel   = 7 for L <= 4096, 15 for L <= 16384, 31 for L <= 65536, else 63
+ * A budget of at least L compresses nothing: keep = L, page_size = 1, r = D, topk = L,
+ * approx_tokens = 0. Requires L >= 1, D >= 1, 1 <= W <= L, token_budget >= 1; every output
+ * pointer non-NULL. Outputs are written only on success.
+ * ------------------------------------------------------------------------------------------ */
+int rkv_plan_budget(int L, int D, int W, int token_budget, int* keep, int* page_size, int* r,
+                    int* topk, int* pool_kernel, int* approx_tokens);
+
+/* ------------------------------------------------------------------------------------------
  * Stage 1 - SnapKV++ permanent eviction ([rebuttal] "Measurement of Exact-TopK": one-time top-k
  * filtering of the prompt; "SCBench Results": driven by the queries at the end of the prompt;
  * "Is Needle Among Evicted Tokens": independent per KV head and layer; [summary] and [rebuttal]

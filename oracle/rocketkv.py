@@ -290,6 +290,38 @@ def mt_view(k, v, kept):
     return k_c, v_c
 
 
+def plan_budget(L: int, D: int, W: int, token_budget: int) -> dict:
+    """Both stages' settings for a token budget (rebuttal, "Is Page Always Divided Into 4?": the
+    ratio L / budget splits evenly between the two stages, and the second stage's share evenly
+    between page size and channel reduction; "Lack of Direct Latency Comparison": the budget
+    counts the approximation's reads, the rest is attended; "Potential Sensitivity to Kernel Size
+    in SnapKV++": longer inputs take larger pooling kernels). Rounding: nearest integer for keep,
+    page size and channels, approximation tokens rounded up, the attended tokens rounded down to
+    whole pages."""
+    import math
+    if L <= 4096:
+        pool = 7
+    elif L <= 16384:
+        pool = 15
+    elif L <= 65536:
+        pool = 31
+    else:
+        pool = 63
+    if token_budget >= L:
+        return dict(keep=L, page_size=1, r=D, topk=L, pool_kernel=pool, approx_tokens=0)
+    per_stage = math.sqrt(L / token_budget)
+    per_dim = math.sqrt(per_stage)
+    keep = min(max(int(math.floor(L / per_stage + 0.5)), W), L)
+    page_size = max(1, int(math.floor(per_dim + 0.5)))
+    r = min(max(int(math.floor(D / per_dim + 0.5)), 1), D)
+    approx = -(-(keep * r) // (page_size * 2 * D))
+    pages_kept = -(-keep // page_size)
+    topk = (token_budget - approx) // page_size * page_size if token_budget > approx else 0
+    topk = min(max(topk, page_size), pages_kept * page_size)
+    return dict(keep=keep, page_size=page_size, r=r, topk=topk, pool_kernel=pool,
+                approx_tokens=approx)
+
+
 def summaries(k_c, page_size: int):
     """page_summaries over a batch: k_c [B,Hkv,Lc,D] -> (kmin_t, kmax_t) [B,Hkv,D,P]."""
     k_c = widen(k_c)

@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     rkv_hybrid_decode_step_cap,
     rkv_build_page_summaries_indexed,
     rkv_hybrid_decode_step_indexed,
+    rkv_plan_budget,
     rkv_hybrid_approx_scores,
     rkv_snapkvpp_evict,
     rkv_sparse_attend_decode,

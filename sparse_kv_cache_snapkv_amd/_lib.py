@@ -14,6 +14,7 @@ _szp = ctypes.POINTER(ctypes.c_size_t)
 SIGNATURES = {
     "rkv_version": (_c_int, []),
     "rkv_status_string": (ctypes.c_char_p, [_c_int]),
+    "rkv_plan_budget": (_c_int, [_c_int] * 4 + [ctypes.POINTER(_c_int)] * 6),
     "rkv_snapkvpp_workspace_bytes": (_c_int, [_c_int] * 8 + [_szp]),
     "rkv_snapkvpp_evict": (_c_int, [_vp, _vp, _vp] + [_c_int] * 9 + [_c_float, _c_int]
                            + [_vp, _vp, _vp, _vp, _vp, _c_size, _vp]),

@@ -312,6 +312,17 @@ def rkv_hybrid_decode_step_cap(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: to
     return out
 
 
+# ----------------------------------------------------------------------------- budget planner
+def rkv_plan_budget(L: int, D: int, W: int, token_budget: int) -> dict:
+    """Settings of both stages for a token budget (host only): keep, page_size, r, topk,
+    pool_kernel, approx_tokens."""
+    outs = [ctypes.c_int(0) for _ in range(6)]
+    _check("rkv_plan_budget", _lib.load().rkv_plan_budget(
+        L, D, W, token_budget, *[ctypes.byref(o) for o in outs]))
+    names = ("keep", "page_size", "r", "topk", "pool_kernel", "approx_tokens")
+    return {n: o.value for n, o in zip(names, outs)}
+
+
 # ----------------------------------------------------------------------------- multi-turn variant
 def _kept_rows(k: torch.Tensor, kept_idx: torch.Tensor) -> int:
     B, Hkv, L, D = k.shape

@@ -2,6 +2,9 @@
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "../../include/rkv.h"
 #include "rkv_launch.hpp"
 
@@ -51,6 +54,39 @@ int check_evict(const void* q_win, const void* k, const void* v, int B, int Hq, 
 extern "C" {
 
 int rkv_version(void) { return RKV_VERSION; }
+
+int rkv_plan_budget(int L, int D, int W, int token_budget, int* keep, int* page_size, int* r,
+                    int* topk, int* pool_kernel, int* approx_tokens) {
+  if (!keep || !page_size || !r || !topk || !pool_kernel || !approx_tokens) return RKV_ERR_NULL;
+  if (L < 1 || D < 1 || W < 1 || W > L || token_budget < 1) return RKV_ERR_SHAPE;
+  const int pool = L <= 4096 ? 7 : L <= 16384 ? 15 : L <= 65536 ? 31 : 63;
+  if (token_budget >= L) {
+    *keep = L;
+    *page_size = 1;
+    *r = D;
+    *topk = L;
+    *pool_kernel = pool;
+    *approx_tokens = 0;
+    return RKV_OK;
+  }
+  const double stage = std::sqrt((double)L / (double)token_budget);  // each stage's ratio
+  const double dim = std::sqrt(stage);  // each dimension's share of the second stage
+  const int kp = std::min(std::max((int)std::lround((double)L / stage), W), L);
+  const int ps = std::max(1, (int)std::lround(dim));
+  const int rr = std::min(std::max((int)std::lround((double)D / dim), 1), D);
+  const long num = (long)kp * rr, den = (long)ps * 2 * D;
+  const int approx = (int)((num + den - 1) / den);
+  const int kcap = ceil_div(kp, ps) * ps;
+  int tk = (token_budget - approx) / ps * ps;
+  tk = std::min(std::max(tk, ps), kcap);
+  *keep = kp;
+  *page_size = ps;
+  *r = rr;
+  *topk = tk;
+  *pool_kernel = pool;
+  *approx_tokens = approx;
+  return RKV_OK;
+}
 
 const char* rkv_status_string(int status) {
   switch (status) {

@@ -161,3 +161,18 @@ def test_decode_calls_reject_bad_arguments(lib):
     assert tk(FAKE, 0, 10, 3, FAKE, None, 0, None) == -2
     assert tk(FAKE, 1, 10, -1, FAKE, None, 0, None) == -2
     assert tk(None, 1, 10, 3, FAKE, None, 0, None) == -1
+
+
+def test_plan_budget_matches_the_oracle(lib):
+    # a host-only call: the library's planner equals the oracle's over a grid of shapes
+    from oracle import rocketkv as O
+    from sparse_kv_cache_snapkv_amd import rkv_plan_budget
+    for L in (1, 7, 100, 2048, 5000, 32768, 131072, 262144):
+        for D in (64, 128):
+            for budget in (1, 16, 128, 256, 512, 1000, 4096, 300000):
+                W = min(32, L)
+                assert rkv_plan_budget(L, D, W, budget) == O.plan_budget(L, D, W, budget), \
+                    (L, D, budget)
+    outs = [ctypes.c_int(-7) for _ in range(6)]
+    assert lib.rkv_plan_budget(100, 64, 101, 10, *[ctypes.byref(o) for o in outs]) == -2
+    assert all(o.value == -7 for o in outs)  # nothing written on error

@@ -428,3 +428,35 @@ def test_widen_bf16_exact():
     assert abs(back[3] - 1e-3) <= 1e-3 * 2 ** -8
     assert np.signbit(back[4])
     assert bits[5] == 0x4780  # 65504 rounds to 65536 in bfloat16
+
+
+# ----------------------------------------------------------------------------- budget planner
+
+def test_plan_budget_rebuttal_worked_example():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "budget_rebuttal_example.json")))
+    e = g["expect"]
+    L, D, W, budget = g["L"], g["D"], g["W"], g["token_budget"]
+    assert L // budget == e["compression_ratio"]
+    assert math.isclose(math.sqrt(L / budget), e["per_stage_ratio"])
+    assert math.isclose(math.sqrt(e["per_stage_ratio"]), e["per_dimension_ratio"])
+    plan = O.plan_budget(L, D, W, budget)
+    for key in ("keep", "page_size", "r", "approx_tokens", "topk"):
+        assert plan[key] == e[key], key
+    assert plan["approx_tokens"] + plan["topk"] == budget  # half approximates, half attends
+
+
+@pytest.mark.parametrize("L,budget", [(2048, 128), (32768, 256), (131072, 1024), (262144, 2048)])
+def test_plan_budget_spends_about_the_budget_and_balances_the_stages(L, budget):
+    # the approximation and the attended tokens add up to the budget (up to rounding to whole
+    # pages), and the first stage's ratio equals the second's (up to rounding)
+    D, W = 128, 32
+    p = O.plan_budget(L, D, W, budget)
+    assert p["topk"] % p["page_size"] == 0
+    assert abs(p["approx_tokens"] + p["topk"] - budget) <= 2 * p["page_size"] + 1
+    s1 = L / p["keep"]
+    s2 = (p["page_size"] * D / p["r"])
+    assert 0.6 < s1 / s2 < 1.7
+    assert O.plan_budget(L, D, W, L)["keep"] == L and O.plan_budget(L, D, W, L)["topk"] == L
