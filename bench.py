@@ -360,6 +360,28 @@ def main() -> int:
         torch.cuda.synchronize()
         grow_us[name] = a0.elapsed_time(a1) * 1e3 / (args.steps * nsteps)
     app_bytes = 8 * B * Hkv * D * w.elem_bytes  # read k_new, v_new; write K, V; min, max RMW
+
+    # ---- outside the timed region: selection quality against Exact-TopK (replica 0, the first
+    # decode steps), RocketKV's split against QUEST-like and SparQ-like settings of the same
+    # approximation ratio (page_size * D / r)
+    from sparse_kv_cache_snapkv_amd import quality
+    ratio = w.page_size * D // w.r
+    settings = dict(hybrid=(w.page_size, w.r), quest_like=(ratio, D), sparq_like=(1, max(1, D // ratio)))
+    qsteps = 4
+    sel_q = {name: {str(tk): dict(recall=0.0, mass=0.0, mass_exact=0.0) for tk in w.topk}
+             for name in settings}
+    for s in range(qsteps):
+        ex = quality.exact_scores(q_dec[s], k_c[0])
+        for name, (ps_q, r_q) in settings.items():
+            for tk in w.topk:
+                m = quality.selection_quality(q_dec[s], k_c[0], ps_q, r_q, tk, scale, exact=ex)
+                for key in m:
+                    sel_q[name][str(tk)][key] += m[key] / qsteps
+    for name in sel_q:
+        for tk in sel_q[name]:
+            sel_q[name][tk] = {k: round(v, 4) for k, v in sel_q[name][tk].items()}
+    sel_q["settings"] = {name: dict(page_size=ps_q, r=r_q) for name, (ps_q, r_q) in settings.items()}
+    sel_q["decode_steps"] = qsteps
     growing = dict(capacity=cap, appends=nsteps, append_us=round(grow_us["append"], 3),
                    append_bytes=app_bytes, append_plus_step_us=round(grow_us["append+step"], 3),
                    step_topk=tk_g, sync_status=rkv.decode_workspace_status(ws_g))
@@ -414,7 +436,8 @@ def main() -> int:
                     context=w.L, window=w.W, pool_kernel=w.pool_kernel, keep=w.keep,
                     page_size=w.page_size, channels=w.r, topk=list(w.topk),
                     decode_steps=nsteps, replicas=R),
-        per_topk=per_topk, stages=stages, growing_cache=growing, roofline=roofline,
+        per_topk=per_topk, stages=stages, growing_cache=growing, selection_quality=sel_q,
+        roofline=roofline,
         sync_status=status,
         wall_ms_timed=round(wall_ms, 1))
     if not args.no_cpu_baseline:

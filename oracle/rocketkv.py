@@ -290,6 +290,37 @@ def mt_view(k, v, kept):
     return k_c, v_c
 
 
+def selection_quality(q, k_c, page_size: int, r: int, topk: int, scale: float) -> dict:
+    """Hybrid selection against Exact-TopK (rebuttal, "Measurement of Exact-TopK": the top tokens
+    by true importance for each head and decoding step). Per (b, query head g): Exact-TopK is the
+    stable top-topk of the exact scores q_g . k_t; the hybrid tokens are those of its group's
+    selected pages. recall = |hybrid & exact| / topk; mass = the share of softmax(scale * scores)
+    on the hybrid tokens; mass_exact = the same on Exact-TopK. Means over (b, g)."""
+    q, k_c = widen(q), widen(k_c)
+    B, Hq, D = q.shape
+    Hkv, Lc = k_c.shape[1], k_c.shape[2]
+    G = Hq // Hkv
+    recall, mass, mass_exact = [], [], []
+    for b in range(B):
+        for h in range(Hkv):
+            kmin, kmax = page_summaries(k_c[b, h], page_size)
+            qg = q[b, h * G:(h + 1) * G]
+            chans, qbar = select_channels(qg, min(r, D))
+            sc = approx_page_scores(qbar, chans, kmin, kmax)
+            pages = select_pages(sc, min(topk // page_size, kmin.shape[1]))
+            hyb = page_tokens(pages, page_size, Lc)
+            for g in range(G):
+                s = k_c[b, h] @ qg[g]
+                exact = stable_topk(s, topk)
+                p = np.exp(scale * (s - s.max()))
+                p /= p.sum()
+                recall.append(len(np.intersect1d(hyb, exact)) / len(exact))
+                mass.append(p[hyb].sum())
+                mass_exact.append(p[exact].sum())
+    return dict(recall=float(np.mean(recall)), mass=float(np.mean(mass)),
+                mass_exact=float(np.mean(mass_exact)))
+
+
 def plan_budget(L: int, D: int, W: int, token_budget: int) -> dict:
     """Both stages' settings for a token budget (rebuttal, "Is Page Always Divided Into 4?": the
     ratio L / budget splits evenly between the two stages, and the second stage's share evenly

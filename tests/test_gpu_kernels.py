@@ -595,3 +595,31 @@ def test_mt_indexed_step_equals_step_on_gathered_cache(rkv, dtype, D, Lc, ps):
                                          1 / math.sqrt(D))
                 assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT[dtype],
                                   f"topk={topk} b{b} h{h}")
+
+
+# ----------------------------------------------------------------------------- selection quality
+
+@pytest.mark.parametrize("ps,r", [(4, 32), (16, 128), (1, 8)],
+                         ids=["hybrid", "quest-like", "sparq-like"])
+def test_selection_quality_matches_oracle(rkv, ps, r):
+    # exact per-head scores from the library equal the oracle's dot products (fp32 sum of exact
+    # bf16 products), and recall / attention mass against Exact-TopK equal the oracle's up to
+    # near-tie flips of the fp32 scores
+    from sparse_kv_cache_snapkv_amd import quality as Q
+    B, Hq, Hkv, D, Lc = 1, 8, 2, 128, 2048
+    g = torch.Generator(device="cuda").manual_seed(61)
+    scale_c = torch.randn((B, Hkv, 1, D), device="cuda", generator=g).exp()
+    k_c = (torch.randn((B, Hkv, Lc, D), device="cuda", generator=g) * scale_c).to(torch.bfloat16)
+    q = _randn((B, Hq, D), g, torch.bfloat16)
+    ex = Q.exact_scores(q, k_c)
+    torch.cuda.synchronize()
+    q64, k64 = O.widen(H(q)), O.widen(H(k_c))
+    G = Hq // Hkv
+    ref = np.stack([np.stack([k64[0, gi // G] @ q64[0, gi] for gi in range(Hq)])])
+    got = ex.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref)), "exact scores"
+    for topk in (64, 256):
+        a = Q.selection_quality(q, k_c, ps, r, topk, exact=ex)
+        b = O.selection_quality(H(q), H(k_c), ps, r, topk, 1 / math.sqrt(D))
+        assert abs(a["recall"] - b["recall"]) <= 1.0 / topk, (topk, a, b)
+        assert abs(a["mass"] - b["mass"]) <= 1e-3 and abs(a["mass_exact"] - b["mass_exact"]) <= 1e-3

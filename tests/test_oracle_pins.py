@@ -460,3 +460,25 @@ def test_plan_budget_spends_about_the_budget_and_balances_the_stages(L, budget):
     s2 = (p["page_size"] * D / p["r"])
     assert 0.6 < s1 / s2 < 1.7
     assert O.plan_budget(L, D, W, L)["keep"] == L and O.plan_budget(L, D, W, L)["topk"] == L
+
+
+# ----------------------------------------------------------------------------- selection quality
+
+def test_selection_quality_exact_topk_maximises_mass_by_brute_force():
+    # Exact-TopK's softmax mass is the largest of every topk-subset (enumerated), and the hybrid
+    # with single-token pages, every channel and one head per group is Exact-TopK itself
+    rng = np.random.default_rng(51)
+    B, Hq, Hkv, Lc, D, topk = 1, 2, 2, 8, 4, 3
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, Lc, D))
+    res = O.selection_quality(q, k, 1, D, topk, 0.7)
+    assert res["recall"] == 1.0 and math.isclose(res["mass"], res["mass_exact"])
+    for h in range(Hkv):
+        s = k[0, h] @ q[0, h]
+        p = np.exp(0.7 * (s - s.max()))
+        p /= p.sum()
+        best = max(p[list(c)].sum() for c in itertools.combinations(range(Lc), topk))
+        assert math.isclose(p[O.stable_topk(s, topk)].sum(), best)
+    coarse = O.selection_quality(q, k, 4, 1, topk + 1, 0.7)
+    assert 0.0 <= coarse["recall"] <= 1.0 and coarse["mass"] <= 1.0 + 1e-12
+    assert O.selection_quality(q, k, 2, D, Lc, 0.7)["mass"] > 1 - 1e-12  # every token selected
