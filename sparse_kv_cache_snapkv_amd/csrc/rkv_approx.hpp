@@ -113,72 +113,103 @@ constexpr int kScoreBatch = kApproxMaxD / kScoreGroups;  // every row load of a 
 // (p_begin and the row pitch multiples of the vector width); otherwise one page per vector.
 // Scores pages [p_begin, p_end) of one (b, h), whose summary rows are `pitch` pages apart, and
 // hands each score to sink(page, value), called by one lane per page. No barrier; the whole row
-// of a vector must be active together.
-template <typename T, bool VEC, typename Sink>
-__device__ __forceinline__ void score_page_range(const T* __restrict__ kmin_bh,
-                                                 const T* __restrict__ kmax_bh, int D, int pitch,
-                                                 int r, int p_begin, int p_end,
-                                                 const ChannelShared& ch, Sink&& sink) {
+// of a vector must be active together. BATCH: row loads a lane can hold per pass (at least the
+// group's channel count, ceil(r / 16)); PASSES: passes whose loads are all issued before the
+// first of them is summed, so a long range keeps PASSES * BATCH loads per lane in flight.
+template <typename T, bool VEC, int BATCH, int PASSES, typename Sink>
+__device__ __forceinline__ void score_pages(const T* __restrict__ kmin_bh,
+                                            const T* __restrict__ kmax_bh, int D, int pitch,
+                                            int r, int p_begin, int p_end,
+                                            const ChannelShared& ch, Sink&& sink) {
   constexpr int V = VEC ? vec16<T>::n : 1;
   const int grp = threadIdx.x % kScoreGroups;
   const int nvec_pass = blockDim.x / kScoreGroups;
   const int nvec = (p_end - p_begin + V - 1) / V;
   const int nj = (r - grp + kScoreGroups - 1) / kScoreGroups;  // channels of this group
-  for (int v0 = 0; v0 < nvec; v0 += nvec_pass) {  // uniform trip count across the block
-    const int vi = v0 + (int)threadIdx.x / kScoreGroups;
-    const bool active = vi < nvec;
-    const int p = p_begin + (active ? vi : 0) * V;
-    float acc[V];
+  // the lane's channel rows (its group's channels grp, grp + 16, ...) and their q-bar factors
+  float qcv[BATCH];
+  const T* rows[BATCH];
 #pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] = 0.f;
-    {
-      // every row load of the lane (at most kScoreBatch, one batch covers r <= kApproxMaxD) is
-      // issued before the first multiply; loads past the group's channel count are not issued
-      float qcv[kScoreBatch];
-      const T* rows[kScoreBatch];
+  for (int u = 0; u < BATCH; ++u) {
+    const int j = grp + (u < nj ? u : 0) * kScoreGroups;
+    qcv[u] = u < nj ? ch.qc[j] : 0.f;
+    const int c = min(max(ch.chan[j], 0), D - 1);
+    rows[u] = (qcv[u] >= 0.f ? kmax_bh : kmin_bh) + (size_t)c * pitch;
+  }
+  for (int v0 = 0; v0 < nvec; v0 += nvec_pass * PASSES) {  // uniform trip count across the block
+    int pg[PASSES];
+    bool act[PASSES];
 #pragma unroll
-      for (int u = 0; u < kScoreBatch; ++u) {
-        const int j = grp + (u < nj ? u : 0) * kScoreGroups;
-        qcv[u] = u < nj ? ch.qc[j] : 0.f;
-        const int c = min(max(ch.chan[j], 0), D - 1);
-        rows[u] = (qcv[u] >= 0.f ? kmax_bh : kmin_bh) + (size_t)c * pitch + p;
-      }
-      if constexpr (VEC) {
-        uint4 raw[kScoreBatch];
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int vi = v0 + ps * nvec_pass + (int)threadIdx.x / kScoreGroups;
+      act[ps] = vi < nvec;
+      pg[ps] = p_begin + (act[ps] ? vi : 0) * V;
+    }
+    if constexpr (VEC) {
+      uint4 raw[PASSES][BATCH];
 #pragma unroll
-        for (int u = 0; u < kScoreBatch; ++u) {
-          raw[u] = make_uint4(0u, 0u, 0u, 0u);
-          if (u < nj) raw[u] = load16(rows[u]);
+      for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          raw[ps][u] = make_uint4(0u, 0u, 0u, 0u);
+          if (u < nj && (ps == 0 || act[ps])) raw[ps][u] = load16(rows[u] + pg[ps]);
         }
 #pragma unroll
-        for (int u = 0; u < kScoreBatch; ++u) {
+      for (int ps = 0; ps < PASSES; ++ps) {
+        if (ps > 0 && v0 + ps * nvec_pass >= nvec) break;  // block-uniform: no vector left
+        float acc[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
           float x[V];
-          unpack16<T>(raw[u], x);
+          unpack16<T>(raw[ps][u], x);
           const bool use = u < nj;
 #pragma unroll
           for (int e = 0; e < V; ++e) acc[e] = use ? fmaf(qcv[u], x[e], acc[e]) : acc[e];
         }
-      } else {
-        float raw[kScoreBatch];
 #pragma unroll
-        for (int u = 0; u < kScoreBatch; ++u) {
-          raw[u] = 0.f;
-          if (u < nj) raw[u] = to_f32(rows[u][0]);
+        for (int e = 0; e < V; ++e) acc[e] = group_sum<kScoreGroups>(acc[e]);
+        if (act[ps]) {
+          // lane `grp` of the row hands over page grp of its vector (all lanes hold the sums)
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            if (e % kScoreGroups == grp && pg[ps] + e < p_end) sink(pg[ps] + e, acc[e]);
+        }
+      }
+    } else {
+      float raw[PASSES][BATCH];
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          raw[ps][u] = 0.f;
+          if (u < nj && (ps == 0 || act[ps])) raw[ps][u] = to_f32(rows[u][pg[ps]]);
         }
 #pragma unroll
-        for (int u = 0; u < kScoreBatch; ++u)
-          acc[0] = u < nj ? fmaf(qcv[u], raw[u], acc[0]) : acc[0];
+      for (int ps = 0; ps < PASSES; ++ps) {
+        if (ps > 0 && v0 + ps * nvec_pass >= nvec) break;
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) acc = u < nj ? fmaf(qcv[u], raw[ps][u], acc) : acc;
+        acc = group_sum<kScoreGroups>(acc);
+        if (act[ps] && grp == 0 && pg[ps] < p_end) sink(pg[ps], acc);
       }
     }
-#pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] = group_sum<kScoreGroups>(acc[e]);
-    if (active) {
-      // lane `grp` of the row hands over page grp of its vector (all lanes hold the sums)
-#pragma unroll
-      for (int e = 0; e < V; ++e)
-        if (e % kScoreGroups == grp && p + e < p_end) sink(p + e, acc[e]);
-    }
   }
+}
+
+// score_pages for any r <= kApproxMaxD; with at most two channels per group (r <= 32) four
+// passes' loads are kept in flight.
+template <typename T, bool VEC, typename Sink>
+__device__ __forceinline__ void score_page_range(const T* __restrict__ kmin_bh,
+                                                 const T* __restrict__ kmax_bh, int D, int pitch,
+                                                 int r, int p_begin, int p_end,
+                                                 const ChannelShared& ch, Sink&& sink) {
+  if (r <= 2 * kScoreGroups)
+    score_pages<T, VEC, 2, 4>(kmin_bh, kmax_bh, D, pitch, r, p_begin, p_end, ch, sink);
+  else
+    score_pages<T, VEC, kScoreBatch, 1>(kmin_bh, kmax_bh, D, pitch, r, p_begin, p_end, ch, sink);
 }
 
 }  // namespace rkv
