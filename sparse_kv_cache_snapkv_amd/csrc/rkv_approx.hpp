@@ -199,14 +199,16 @@ __device__ __forceinline__ void score_pages(const T* __restrict__ kmin_bh,
   }
 }
 
-// score_pages for any r <= kApproxMaxD; with at most two channels per group (r <= 32) four
-// passes' loads are kept in flight.
+// score_pages for any r <= kApproxMaxD; a range of more than one pass with at most two channels
+// per group (r <= 32) keeps four passes' loads in flight.
 template <typename T, bool VEC, typename Sink>
 __device__ __forceinline__ void score_page_range(const T* __restrict__ kmin_bh,
                                                  const T* __restrict__ kmax_bh, int D, int pitch,
                                                  int r, int p_begin, int p_end,
                                                  const ChannelShared& ch, Sink&& sink) {
-  if (r <= 2 * kScoreGroups)
+  constexpr int V = VEC ? vec16<T>::n : 1;
+  const bool long_range = p_end - p_begin > (int)(blockDim.x / kScoreGroups) * V;
+  if (r <= 2 * kScoreGroups && long_range)
     score_pages<T, VEC, 2, 4>(kmin_bh, kmax_bh, D, pitch, r, p_begin, p_end, ch, sink);
   else
     score_pages<T, VEC, kScoreBatch, 1>(kmin_bh, kmax_bh, D, pitch, r, p_begin, p_end, ch, sink);
