@@ -261,6 +261,9 @@ def main() -> int:
                    [(f"split_topk@{tk}", (lambda tk=tk: topk_all(tk))) for tk in w.topk] + \
                    [(f"split_attend@{tk}", (lambda tk=tk: attend_all(tk))) for tk in w.topk]
     side = torch.cuda.Stream()
+    # inputs, summaries and workspaces (with their zero-fill) were made on the default stream: the
+    # warm-up on the side stream may only start once they exist
+    torch.cuda.synchronize()
     with torch.cuda.stream(side):
         for _, fn in stages + split_stages:
             fn()
@@ -344,7 +347,9 @@ def main() -> int:
                                            workspace=ws_g)
 
     grow_us = {}
+    torch.cuda.synchronize()  # the grown caches and their workspace exist before the side stream
     for name, fn in (("append", append_all), ("append+step", grow_all)):
+        torch.cuda.synchronize()
         with torch.cuda.stream(side):
             fn()
         torch.cuda.synchronize()
