@@ -19,8 +19,11 @@ LIB = os.path.join(PKG, "librkv.so")
 ARCH = "gfx950"
 # Packed fp32 ops are disabled for every HIP translation unit (the host pass warns that it does
 # not know the feature; that is harmless).
+# MFMA results go to ordinary VGPRs rather than accumulation registers: the window passes of the
+# eviction read every result with VALU code, which would otherwise first copy it out.
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -29,6 +29,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kKeysPerSub = 256;  // 4 waves x 64 keys
+constexpr int kPassBlocks = 512;  // blocks per window-pass launch: two per CU, all resident
 
 inline int round32(int x) { return (x + 31) & ~31; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -46,7 +47,7 @@ EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int keep, int dtype
   lo.nprefix = L - W;
   auto split = [&](int nkeys, int& nchunk, int& nsub) {
     const int subs = (nkeys + kKeysPerSub - 1) / kKeysPerSub;
-    int want = (512 + BH - 1) / BH;  // about two blocks per CU overall
+    int want = (kPassBlocks + BH - 1) / BH;
     if (want > subs) want = subs;
     if (want < 1) want = 1;
     nsub = (subs + want - 1) / want;
@@ -91,11 +92,35 @@ __device__ __forceinline__ void load_key_tiles(const bf16_t* __restrict__ k_bh, 
   }
 }
 
+// Window rows of one head into LDS (row pitch D + 8, rows GW..GWp-1 zero), eight 16-byte loads
+// per thread in flight at a time.
+template <int D>
+__device__ __forceinline__ void stage_window_rows(uint16_t* smem, const bf16_t* __restrict__ qg,
+                                                  int GW, int GWp, int tid) {
+  constexpr int QS = D + 8, kBatch = 8;
+  const int n16 = GWp * (D / 8);
+  for (int base = 0; base < n16; base += kBatch * kThreads) {
+    uint4 val[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = base + j * kThreads + tid, row = idx / (D / 8), c8 = idx % (D / 8);
+      val[j] = make_uint4(0, 0, 0, 0);
+      if (row < GW) val[j] = load16(qg + (size_t)row * D + c8 * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = base + j * kThreads + tid, row = idx / (D / 8), c8 = idx % (D / 8);
+      if (idx < n16) *reinterpret_cast<uint4*>(smem + (size_t)row * QS + c8 * 8) = val[j];
+    }
+  }
+}
+
 // Pass 1: per window row, the running (max, sum of exp2) of its scaled logits over this block's
 // keys, in log2 units. Each lane keeps the running pair of its row in every 32-row tile across
 // all of the block's key groups; the pairs of the lane halves and the four waves merge once at
-// the end.
-template <int D>
+// the end. MT is the most 32-row tiles the kernel takes (GW <= 32 * MT): the running pairs of
+// every tile stay in registers.
+template <int D, int MT>
 __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __restrict__ q_win,
                                                              const bf16_t* __restrict__ k, int L,
                                                              int W, int GW, int nsub, int nchunk,
@@ -103,20 +128,23 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
                                                              float2* __restrict__ stats) {
   constexpr int KS = D / 16;
   constexpr int QS = D + 8;
-  constexpr int kMaxTiles = 16;  // GW <= 512
+  constexpr int kMaxTiles = MT;
   extern __shared__ __align__(16) uint16_t smem[];
   const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y, chunk = blockIdx.x;
   float2* wst = reinterpret_cast<float2*>(smem + (size_t)GWp * QS);  // [4][GWp]
 
-  const bf16_t* qg = q_win + (size_t)bh * GW * D;
-  for (int idx = tid; idx < GWp * (D / 8); idx += kThreads) {
-    const int row = idx / (D / 8), c8 = idx % (D / 8);
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (row < GW) val = load16(qg + (size_t)row * D + c8 * 8);
-    *reinterpret_cast<uint4*>(smem + (size_t)row * QS + c8 * 8) = val;
-  }
+  // Key groups are interleaved over the chunks (group j of chunk c starts at key
+  // (j * nchunk + c) * 256), so the blocks of a head sweep its keys as one front. Key registers
+  // are double-buffered: the next group's loads are in flight while the current one is
+  // multiplied. The first group's loads go out before the window rows are staged.
+  const bf16_t* k_bh = k + (size_t)bh * L * D;
+  auto key_of = [&](int t) { return (t * nchunk + chunk) * kKeysPerSub + wave * 64; };
+  bf16x8 kf0[2][KS], kf1[2][KS];
+  load_key_tiles<D>(k_bh, key_of(0), L - 1, hf, n, kf0);
+
+  stage_window_rows<D>(smem, q_win + (size_t)bh * GW * D, GW, GWp, tid);
   __syncthreads();
 
   float m[kMaxTiles], l[kMaxTiles];
@@ -125,12 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
     m[rt] = -INFINITY;
     l[rt] = 0.f;
   }
-  const bf16_t* k_bh = k + (size_t)bh * L * D;
-  const int first = chunk * nsub * kKeysPerSub + wave * 64;
-  bf16x8 kf[2][KS];
-  load_key_tiles<D>(k_bh, first, L - 1, hf, n, kf);
-  for (int sub = 0; sub < nsub; ++sub) {
-    const int key0 = first + sub * kKeysPerSub;
+  auto group_stats = [&](const bf16x8(&kf)[2][KS], int key0) {
     // keys below L-W are visible to every window row: only groups reaching it need the mask
     const bool masked = key0 + 63 >= L - W;
 #pragma unroll
@@ -176,7 +199,17 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
         m[rt] = mn;
       }
     }
-    if (sub + 1 < nsub) load_key_tiles<D>(k_bh, key0 + kKeysPerSub, L - 1, hf, n, kf);
+  };
+  // The next group's loads always go out (past the chunk's last group they re-read the current
+  // rows, from cache): issued on some paths only, the compiler's wait for the current group
+  // would also cover them.
+  for (int t = 0; t < nsub; t += 2) {
+    const int key0 = key_of(t), key1 = t + 1 < nsub ? key_of(t + 1) : key0;
+    load_key_tiles<D>(k_bh, key1, L - 1, hf, n, kf1);
+    group_stats(kf0, key0);
+    if (t + 1 >= nsub) break;
+    load_key_tiles<D>(k_bh, t + 2 < nsub ? key_of(t + 2) : key1, L - 1, hf, n, kf0);
+    group_stats(kf1, key1);
   }
   // merge the two lane halves (same rows, other keys), then the waves through LDS
 #pragma unroll
@@ -211,41 +244,34 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
                                                               const bf16_t* __restrict__ k,
                                                               const float* __restrict__ lse,
                                                               int L, int W, int GW, int nsub,
-                                                              float scale2,
+                                                              int nchunk, float scale2,
                                                               float* __restrict__ colsum) {
   constexpr int KS = D / 16;
   constexpr int QS = D + 8;
   extern __shared__ __align__(16) uint16_t smem[];
   const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
-  // blocks walk the keys in the reverse of pass 1's order: the K rows pass 1 read last are the
-  // ones still held by the Infinity Cache when this pass starts
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int nprefix = L - W;
   float* s_lse = reinterpret_cast<float*>(smem + (size_t)GWp * QS);
 
-  const bf16_t* qg = q_win + (size_t)bh * GW * D;
-  for (int idx = tid; idx < GWp * (D / 8); idx += kThreads) {
-    const int row = idx / (D / 8), c8 = idx % (D / 8);
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (row < GW) val = load16(qg + (size_t)row * D + c8 * 8);
-    *reinterpret_cast<uint4*>(smem + (size_t)row * QS + c8 * 8) = val;
-  }
+  // Key groups interleaved over the chunks and double-buffered as in pass 1, but visited in the
+  // reverse of pass 1's order: the groups pass 1 read last are the likeliest to still be held by
+  // the Infinity Cache. Keys past the prefix are loaded clamped (the prefix is never empty when
+  // the passes run, as keep < L and W <= keep) and never written.
+  const bf16_t* k_bh = k + (size_t)bh * L * D;
+  auto key_of = [&](int t) { return ((nsub - 1 - t) * nchunk + chunk) * kKeysPerSub + wave * 64; };
+  bf16x8 kf0[2][KS], kf1[2][KS];
+  load_key_tiles<D>(k_bh, key_of(0), nprefix - 1, hf, n, kf0);
+
+  stage_window_rows<D>(smem, q_win + (size_t)bh * GW * D, GW, GWp, tid);
   for (int r = tid; r < GWp; r += kThreads) {
     const float x = lse[(size_t)bh * GWp + min(r, GW - 1)];
     s_lse[r] = r < GW ? x : INFINITY;  // padded rows add exp2(-inf) = 0
   }
   __syncthreads();
 
-  const bf16_t* k_bh = k + (size_t)bh * L * D;
-  const int first = chunk * nsub * kKeysPerSub + wave * 64;
-  if (first >= nprefix) return;  // no barrier below: waves may leave independently
-  bf16x8 kf[2][KS];
-  load_key_tiles<D>(k_bh, first, nprefix - 1, hf, n, kf);
-  for (int sub = 0; sub < nsub; ++sub) {
-    const int key0 = first + sub * kKeysPerSub;
-    if (key0 >= nprefix) break;
-    const bool more = sub + 1 < nsub && key0 + kKeysPerSub < nprefix;
+  auto group_colsum = [&](const bf16x8(&kf)[2][KS], int key0) {
     float cs[2] = {0.f, 0.f};
     for (int rt = 0; rt < NRT; ++rt) {
       f32x16 acc[2];
@@ -274,7 +300,14 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
       const int key = key0 + kt * 32 + n;
       if (hf == 0 && key < nprefix) colsum[(size_t)bh * nprefix + key] = tot;
     }
-    if (more) load_key_tiles<D>(k_bh, key0 + kKeysPerSub, nprefix - 1, hf, n, kf);
+  };
+  for (int t = 0; t < nsub; t += 2) {  // the next group's loads always go out, as in pass 1
+    const int key0 = key_of(t), key1 = t + 1 < nsub ? key_of(t + 1) : key0;
+    load_key_tiles<D>(k_bh, key1, nprefix - 1, hf, n, kf1);
+    group_colsum(kf0, key0);
+    if (t + 1 >= nsub) break;
+    load_key_tiles<D>(k_bh, t + 2 < nsub ? key_of(t + 2) : key1, nprefix - 1, hf, n, kf0);
+    group_colsum(kf1, key1);
   }
 }
 
@@ -365,9 +398,16 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_f32(const float* __rest
 // ---------------------------------------------------------------------------- shared stages
 
 // Per window row, the log2-sum-exp of its scaled logits from the pass-1 chunk pairs: one wave per
-// row, lanes over chunks (online merge per lane), then a wave-wide merge.
+// row, lanes over chunks (online merge per lane), then a wave-wide merge. The grid also clears
+// the nzero words at zero (the kept-set top-k's digit histograms).
 __global__ __launch_bounds__(kThreads) void k_win_lse(const float2* __restrict__ stats, int nchunk,
-                                                      int GW, float* __restrict__ lse) {
+                                                      int GW, float* __restrict__ lse,
+                                                      uint32_t* __restrict__ zero, int nzero) {
+  {
+    const int nthr = gridDim.x * gridDim.y * kThreads;
+    const int t0 = (blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+    for (int i = t0; i < nzero; i += nthr) zero[i] = 0u;
+  }
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int r = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
@@ -473,38 +513,51 @@ hipError_t gather_any(int dtype, int D, const void* k, const void* v, int BH, in
                  : gather<bf16_t, 128>(k, v, BH, L, W, Lc, identity, kept, k_out, v_out, stream);
 }
 
-template <int D>
+template <int D, int MT>
 hipError_t scores_bf16(const void* q_win, const void* k, int BH, int L, int W,
-                       const EvictLayout& lo, float scale2, char* ws, hipStream_t stream) {
+                       const EvictLayout& lo, float scale2, char* ws, uint32_t* zero, int nzero,
+                       hipStream_t stream) {
   constexpr int QS = D + 8;
   float2* stats = reinterpret_cast<float2*>(ws + lo.off_stats);
   float* lse = reinterpret_cast<float*>(ws + lo.off_lse);
   float* colsum = reinterpret_cast<float*>(ws + lo.off_colsum);
-  const size_t lds1 = (size_t)lo.GWp * QS * 2 + (size_t)lo.GWp * sizeof(float2) * 5;
+  const size_t lds1 = (size_t)lo.GWp * QS * 2 + (size_t)lo.GWp * sizeof(float2) * 4;
   const size_t lds2 = (size_t)lo.GWp * QS * 2 + (size_t)lo.GWp * sizeof(float);
-  if (lds1 > 64 * 1024)
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_stats_mfma<D>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
-  if (lds2 > 64 * 1024)
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_colsum_mfma<D>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
-  hipLaunchKernelGGL(k_win_stats_mfma<D>, dim3(lo.nchunk1, BH), dim3(kThreads), lds1, stream,
-                     static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), L, W,
-                     lo.GW, lo.nsub1, lo.nchunk1, scale2, stats);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (lds1 > 64 * 1024 &&
+      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_stats_mfma<D, MT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1)) != hipSuccess)
+    return e;
+  if (lds2 > 64 * 1024 &&
+      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_colsum_mfma<D>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL((k_win_stats_mfma<D, MT>), dim3(lo.nchunk1, BH), dim3(kThreads), lds1, stream,
+                     static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), L, W, lo.GW,
+                     lo.nsub1, lo.nchunk1, scale2, stats);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_win_lse, dim3((lo.GW + 3) / 4, BH), dim3(kThreads), 0, stream, stats,
-                     lo.nchunk1, lo.GW, lse);
+                     lo.nchunk1, lo.GW, lse, zero, nzero);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_win_colsum_mfma<D>, dim3(lo.nchunk2, BH), dim3(kThreads), lds2, stream,
                      static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), lse, L, W,
-                     lo.GW, lo.nsub2, scale2, colsum);
+                     lo.GW, lo.nsub2, lo.nchunk2, scale2, colsum);
   return hipGetLastError();
 }
 
 template <int D>
+hipError_t scores_bf16_any(const void* q_win, const void* k, int BH, int L, int W,
+                           const EvictLayout& lo, float scale2, char* ws, uint32_t* zero,
+                           int nzero, hipStream_t stream) {
+  return lo.GWp <= 128
+             ? scores_bf16<D, 4>(q_win, k, BH, L, W, lo, scale2, ws, zero, nzero, stream)
+             : scores_bf16<D, 16>(q_win, k, BH, L, W, lo, scale2, ws, zero, nzero, stream);
+}
+
+template <int D>
 hipError_t scores_f32(const void* q_win, const void* k, int BH, int L, int W,
-                      const EvictLayout& lo, float scale2, char* ws, hipStream_t stream) {
+                      const EvictLayout& lo, float scale2, char* ws, uint32_t* zero, int nzero,
+                      hipStream_t stream) {
   float2* stats = reinterpret_cast<float2*>(ws + lo.off_stats);
   float* lse = reinterpret_cast<float*>(ws + lo.off_lse);
   float* colsum = reinterpret_cast<float*>(ws + lo.off_colsum);
@@ -515,7 +568,7 @@ hipError_t scores_f32(const void* q_win, const void* k, int BH, int L, int W,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_win_lse, dim3((lo.GW + 3) / 4, BH), dim3(kThreads), 0, stream, stats,
-                     nchunk, lo.GW, lse);
+                     nchunk, lo.GW, lse, zero, nzero);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_win_colsum_f32<D>, dim3((lo.nprefix + kThreads - 1) / kThreads, BH),
                      dim3(kThreads), 0, stream, static_cast<const float*>(q_win),
@@ -526,8 +579,8 @@ hipError_t scores_f32(const void* q_win, const void* k, int BH, int L, int W,
 }  // namespace
 
 size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype) {
-  (void)D;
   if (keep >= L) return 0;
+  (void)D;
   return layout_for(B, Hq, Hkv, L, W, keep, dtype).total;
 }
 
@@ -541,15 +594,20 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
   const EvictLayout lo = layout_for(B, Hq, Hkv, L, W, keep, dtype);
   char* w = static_cast<char*>(ws);
   const float scale2 = scale * kLog2e;
+  const int n = lo.nprefix;
+  // Rows the top-k spreads over blocks have their digit histograms (at the start of the top-k
+  // workspace) cleared by the log-sum-exp launch, which saves the top-k its clearing launch.
+  const bool cleared = topk_multiblock(n, keep - W);
+  uint32_t* hist = cleared ? reinterpret_cast<uint32_t*>(w + lo.off_topk) : nullptr;
+  const int nhist = cleared ? (int)topk_hist_words(BH) : 0;
   hipError_t e;
   if (dtype == 0)
-    e = D == 64 ? scores_f32<64>(q_win, k, BH, L, W, lo, scale2, w, stream)
-                : scores_f32<128>(q_win, k, BH, L, W, lo, scale2, w, stream);
+    e = D == 64 ? scores_f32<64>(q_win, k, BH, L, W, lo, scale2, w, hist, nhist, stream)
+                : scores_f32<128>(q_win, k, BH, L, W, lo, scale2, w, hist, nhist, stream);
   else
-    e = D == 64 ? scores_bf16<64>(q_win, k, BH, L, W, lo, scale2, w, stream)
-                : scores_bf16<128>(q_win, k, BH, L, W, lo, scale2, w, stream);
+    e = D == 64 ? scores_bf16_any<64>(q_win, k, BH, L, W, lo, scale2, w, hist, nhist, stream)
+                : scores_bf16_any<128>(q_win, k, BH, L, W, lo, scale2, w, hist, nhist, stream);
   if (e != hipSuccess) return e;
-  const int n = lo.nprefix;
   float* colsum = reinterpret_cast<float*>(w + lo.off_colsum);
   float* pooled = pooled_out != nullptr ? pooled_out : reinterpret_cast<float*>(w + lo.off_pooled);
   if (pool_type == 0)
@@ -559,9 +617,10 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
     hipLaunchKernelGGL(k_pool<1>, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0,
                        stream, colsum, n, pool_kernel, pooled);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_topk(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk, stream)) !=
-      hipSuccess)
-    return e;
+  e = cleared ? launch_topk_cleared(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk,
+                                    stream)
+              : launch_topk(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk, stream);
+  if (e != hipSuccess) return e;
   return gather_any(dtype, D, k, v, BH, L, W, keep, 0, kept_idx, k_out, v_out, stream);
 }
 

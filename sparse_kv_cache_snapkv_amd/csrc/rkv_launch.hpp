@@ -28,6 +28,14 @@ hipError_t launch_approx_scores(const void* q, const void* kmin_t, const void* k
 size_t topk_ws_bytes(int rows, int n, int k);
 hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out, int out_stride,
                        void* ws, hipStream_t stream);
+// Rows that take the multi-block path keep their digit histograms in the first
+// topk_hist_words(rows) 32-bit words of the top-k workspace. A caller that has already cleared
+// them (in a launch of its own, as SnapKV++ eviction does) calls launch_topk_cleared, which skips
+// the clearing launch.
+bool topk_multiblock(int n, int k);
+size_t topk_hist_words(int rows);
+hipError_t launch_topk_cleared(const float* scores, int rows, int n, int k, int32_t* out,
+                               int out_stride, void* ws, hipStream_t stream);
 
 // Exact attention over the selected pages.
 size_t attend_ws_bytes(int B, int Hq, int Hkv, int D, int page_size, int n_pages, int dtype);

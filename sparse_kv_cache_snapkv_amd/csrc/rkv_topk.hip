@@ -244,6 +244,49 @@ size_t topk_ws_bytes(int rows, int n, int k) {
   return long_path(n, k) ? long_layout(rows, n).total : 0;
 }
 
+bool topk_multiblock(int n, int k) { return long_path(n, k); }
+size_t topk_hist_words(int rows) { return (size_t)rows * kLevels * kHistStride; }
+
+namespace {
+
+// The launches of the multi-block path; the clearing launch only where the histograms are not
+// already zero.
+hipError_t long_launches(const float* scores, int rows, int n, int k, int32_t* out,
+                         int out_stride, void* ws, bool cleared, hipStream_t stream) {
+  const LongLayout lo = long_layout(rows, n);
+  char* w = static_cast<char*>(ws);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(w + lo.off_hist);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + lo.off_cnt);
+  uint32_t* thr = reinterpret_cast<uint32_t*>(w + lo.off_thr);
+  const dim3 lgrid(lo.nblk, rows);
+  hipError_t e;
+  if (!cleared) {
+    const size_t nhist = topk_hist_words(rows);
+    hipLaunchKernelGGL(k_long_zero, dim3((unsigned)std::min<size_t>((nhist + 255) / 256, 1024)),
+                       dim3(256), 0, stream, hist, nhist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_long_hist<0>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_hist<1>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_hist<2>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_count, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist, cnt,
+                     thr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_long_write, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, cnt, thr,
+                     out, out_stride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk_cleared(const float* scores, int rows, int n, int k, int32_t* out,
+                               int out_stride, void* ws, hipStream_t stream) {
+  return long_launches(scores, rows, n, k, out, out_stride, ws, true, stream);
+}
+
 hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out, int out_stride,
                        void* ws, hipStream_t stream) {
   dim3 grid(rows);
@@ -263,29 +306,7 @@ hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out
                        dim3(kBlockThreads), 0, stream, out, n, out_stride);
     return hipGetLastError();
   }
-  const LongLayout lo = long_layout(rows, n);
-  char* w = static_cast<char*>(ws);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(w + lo.off_hist);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + lo.off_cnt);
-  uint32_t* thr = reinterpret_cast<uint32_t*>(w + lo.off_thr);
-  const size_t nhist = (size_t)rows * kLevels * kHistStride;
-  hipLaunchKernelGGL(k_long_zero, dim3((unsigned)std::min<size_t>((nhist + 255) / 256, 1024)),
-                     dim3(256), 0, stream, hist, nhist);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 lgrid(lo.nblk, rows);
-  hipLaunchKernelGGL(k_long_hist<0>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_hist<1>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_hist<2>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_count, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist, cnt,
-                     thr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_write, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, cnt, thr,
-                     out, out_stride);
-  return hipGetLastError();
+  return long_launches(scores, rows, n, k, out, out_stride, ws, false, stream);
 }
 
 }  // namespace rkv
