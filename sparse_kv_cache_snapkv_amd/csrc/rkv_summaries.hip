@@ -10,13 +10,16 @@ namespace rkv {
 
 namespace {
 
-constexpr int kPagesPerBlock = 64;
+constexpr int kPagesPerBlock = 32;
 constexpr int kThreads = 256;
 
 // One block: kPagesPerBlock pages of one (b, h). Reads token rows as 16-byte chunks, reduces
 // over each page's slots, transposes through LDS and writes [D][pages] rows. The cache holds
 // kv_pitch token slots per head (the first Lc valid) and a summary row s_pitch pages. rows (may
 // be null): slot t of head bh is row rows[bh*Lc + t] of the cache, clamped into [0, kv_pitch).
+// A thread owns kItems (page, chunk) items; the loads of kSlots slots of all of them are issued
+// before any is folded (the slots of a page fold in slot order, keeping the first of equal
+// values, as the append does).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ k_c,
                                                           const int32_t* __restrict__ rows,
@@ -25,45 +28,98 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
                                                           int ps, int kv_pitch, int s_pitch) {
   constexpr int V = vec16<T>::n;
   constexpr int CH = D / V;  // 16-byte chunks per token row
+  constexpr int kItems = kPagesPerBlock * CH / kThreads;
+  constexpr int kSlots = 4;
+  static_assert(kItems * kThreads == kPagesPerBlock * CH, "items must tile the block");
   __shared__ float smin[D][kPagesPerBlock + 1];
   __shared__ float smax[D][kPagesPerBlock + 1];
   const int bh = blockIdx.y;
   const int p0 = blockIdx.x * kPagesPerBlock;
   const T* kb = k_c + (size_t)bh * kv_pitch * D;
   const int32_t* rb = rows != nullptr ? rows + (size_t)bh * Lc : nullptr;
-  auto row = [&](int t) { return rb != nullptr ? min(max(rb[t], 0), kv_pitch - 1) : t; };
-  for (int idx = threadIdx.x; idx < kPagesPerBlock * CH; idx += kThreads) {
-    const int pl = idx / CH, ch = idx % CH, p = p0 + pl;
-    if (p >= P) continue;
-    const int t0 = p * ps, t1 = min(t0 + ps, Lc);
-    float mn[V], mx[V];
-    unpack16<T>(load16(kb + (size_t)row(t0) * D + ch * V), mn);
+  int t0[kItems], nt[kItems];
+  float mn[kItems][V], mx[kItems][V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) mx[e] = mn[e];
-    for (int t = t0 + 1; t < t1; ++t) {
-      float x[V];
-      unpack16<T>(load16(kb + (size_t)row(t) * D + ch * V), x);
+  for (int i = 0; i < kItems; ++i) {
+    const int p = p0 + (i * kThreads + threadIdx.x) / CH;
+    t0[i] = p * ps;
+    nt[i] = p < P ? min(ps, Lc - t0[i]) : 0;  // >= 1 for a page of the cache
+  }
+  for (int base = 0; base < ps; base += kSlots) {
+    uint4 raw[kItems][kSlots];
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        mn[e] = x[e] < mn[e] ? x[e] : mn[e];
-        mx[e] = x[e] > mx[e] ? x[e] : mx[e];
+    for (int i = 0; i < kItems; ++i) {
+      const int ch = (i * kThreads + threadIdx.x) % CH;
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        raw[i][s] = make_uint4(0, 0, 0, 0);
+        if (base + s < nt[i]) {
+          const int t = t0[i] + base + s;
+          const int r = rb != nullptr ? min(max(rb[t], 0), kv_pitch - 1) : t;
+          raw[i][s] = load16(kb + (size_t)r * D + ch * V);
+        }
       }
     }
 #pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        if (base + s >= nt[i]) continue;
+        float x[V];
+        unpack16<T>(raw[i][s], x);
+        if (base + s == 0) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) mn[i][e] = mx[i][e] = x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            mn[i][e] = x[e] < mn[i][e] ? x[e] : mn[i][e];
+            mx[i][e] = x[e] > mx[i][e] ? x[e] : mx[i][e];
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    if (nt[i] <= 0) continue;
+    const int idx = i * kThreads + threadIdx.x, pl = idx / CH, ch = idx % CH;
+#pragma unroll
     for (int e = 0; e < V; ++e) {
-      smin[ch * V + e][pl] = mn[e];
-      smax[ch * V + e][pl] = mx[e];
+      smin[ch * V + e][pl] = mn[i][e];
+      smax[ch * V + e][pl] = mx[i][e];
     }
   }
   __syncthreads();
+  // each thread writes kVecP consecutive pages of a channel row with one 16-byte store where the
+  // row segment is whole and aligned (element stores otherwise)
+  constexpr int kVecP = 16 / sizeof(T), kSegs = kPagesPerBlock / kVecP;
   const int np = min(kPagesPerBlock, P - p0);
   T* mnb = kmin_t + (size_t)bh * D * s_pitch + p0;
   T* mxb = kmax_t + (size_t)bh * D * s_pitch + p0;
-  for (int idx = threadIdx.x; idx < D * kPagesPerBlock; idx += kThreads) {
-    const int c = idx / kPagesPerBlock, pl = idx % kPagesPerBlock;
-    if (pl >= np) continue;
-    mnb[(size_t)c * s_pitch + pl] = from_f32<T>(smin[c][pl]);
-    mxb[(size_t)c * s_pitch + pl] = from_f32<T>(smax[c][pl]);
+  for (int idx = threadIdx.x; idx < D * kSegs; idx += kThreads) {
+    const int c = idx / kSegs, pv = (idx % kSegs) * kVecP;
+    if (pv >= np) continue;
+    T* dmn = mnb + (size_t)c * s_pitch + pv;
+    T* dmx = mxb + (size_t)c * s_pitch + pv;
+    if (pv + kVecP <= np && ((reinterpret_cast<uintptr_t>(dmn) | reinterpret_cast<uintptr_t>(dmx)) & 15) == 0) {
+      T vmn[kVecP], vmx[kVecP];
+#pragma unroll
+      for (int e = 0; e < kVecP; ++e) {
+        vmn[e] = from_f32<T>(smin[c][pv + e]);
+        vmx[e] = from_f32<T>(smax[c][pv + e]);
+      }
+      uint4 wmn, wmx;
+      __builtin_memcpy(&wmn, vmn, 16);
+      __builtin_memcpy(&wmx, vmx, 16);
+      *reinterpret_cast<uint4*>(dmn) = wmn;
+      *reinterpret_cast<uint4*>(dmx) = wmx;
+    } else {
+      for (int e = 0; e < kVecP && pv + e < np; ++e) {
+        dmn[e] = from_f32<T>(smin[c][pv + e]);
+        dmx[e] = from_f32<T>(smax[c][pv + e]);
+      }
+    }
   }
 }
 
