@@ -260,6 +260,21 @@ def test_snapkvpp_evict_max_pool_and_limits(rkv):
     _evict_check(rkv, w.replace(keep=w.L + 5), d)      # budget above the prompt
 
 
+def test_snapkvpp_evict_odd_key_groups_multiblock_topk(rkv):
+    # 32 heads over 10000 keys: three key groups per block in both window passes (the last one
+    # unpaired in the double buffer, chunks of different group counts), and a prefix above 8192
+    # scores, so the kept-set top-k spreads each row over blocks with histograms that the
+    # log-sum-exp launch cleared
+    w = configs.SMALL[1].replace(name="odd-groups", B=16, Hq=4, Hkv=2, D=64, L=10000, W=16,
+                                 keep=2000, pool_kernel=15, cfg_id=31)
+    d = gen.prompt_layer(w)
+    _evict_check(rkv, w, d)
+    _evict_check(rkv, w.replace(keep=w.W), d, needles=False)  # nothing to select
+    # the fp32 passes ahead of the same multi-block top-k
+    wf = w.replace(name="odd-groups-fp32", dtype="fp32", B=2, L=9000, cfg_id=32)
+    _evict_check(rkv, wf, gen.prompt_layer(wf))
+
+
 def test_evict_indices_only(rkv):
     w = configs.TINY_FP32
     d = gen.prompt_layer(w)
