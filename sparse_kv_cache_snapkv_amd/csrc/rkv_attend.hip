@@ -677,7 +677,8 @@ Plan plan_attend(int BH, int ps, int n_pages) {
   const int ntok = n_pages * ps;
   const int chunk = kWavesPerBlock * Geo<T, D>::WTOK;
   int ns = (2 * kTargetBlocks + BH - 1) / BH;
-  ns = min(ns, (ntok + chunk - 1) / chunk);
+  // a small budget goes to one block per head: its output is written without a merge launch
+  ns = ntok <= kStepSoloTokens ? 1 : min(ns, (ntok + chunk - 1) / chunk);
   ns = max(ns, (n_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit);
   ns = max(min(ns, 256), 1);
   int pps = (n_pages + ns - 1) / ns;
