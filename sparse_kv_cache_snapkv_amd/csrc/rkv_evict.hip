@@ -402,11 +402,11 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_f32(const float* __rest
 // the nzero words at zero (the kept-set top-k's digit histograms).
 __global__ __launch_bounds__(kThreads) void k_win_lse(const float2* __restrict__ stats, int nchunk,
                                                       int GW, float* __restrict__ lse,
-                                                      uint32_t* __restrict__ zero, int nzero) {
+                                                      uint32_t* __restrict__ zero, size_t nzero) {
   {
-    const int nthr = gridDim.x * gridDim.y * kThreads;
-    const int t0 = (blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
-    for (int i = t0; i < nzero; i += nthr) zero[i] = 0u;
+    const size_t nthr = (size_t)gridDim.x * gridDim.y * kThreads;
+    const size_t t0 = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+    for (size_t i = t0; i < nzero; i += nthr) zero[i] = 0u;
   }
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -515,7 +515,7 @@ hipError_t gather_any(int dtype, int D, const void* k, const void* v, int BH, in
 
 template <int D, int MT>
 hipError_t scores_bf16(const void* q_win, const void* k, int BH, int L, int W,
-                       const EvictLayout& lo, float scale2, char* ws, uint32_t* zero, int nzero,
+                       const EvictLayout& lo, float scale2, char* ws, uint32_t* zero, size_t nzero,
                        hipStream_t stream) {
   constexpr int QS = D + 8;
   float2* stats = reinterpret_cast<float2*>(ws + lo.off_stats);
@@ -548,7 +548,7 @@ hipError_t scores_bf16(const void* q_win, const void* k, int BH, int L, int W,
 template <int D>
 hipError_t scores_bf16_any(const void* q_win, const void* k, int BH, int L, int W,
                            const EvictLayout& lo, float scale2, char* ws, uint32_t* zero,
-                           int nzero, hipStream_t stream) {
+                           size_t nzero, hipStream_t stream) {
   return lo.GWp <= 128
              ? scores_bf16<D, 4>(q_win, k, BH, L, W, lo, scale2, ws, zero, nzero, stream)
              : scores_bf16<D, 16>(q_win, k, BH, L, W, lo, scale2, ws, zero, nzero, stream);
@@ -556,7 +556,7 @@ hipError_t scores_bf16_any(const void* q_win, const void* k, int BH, int L, int 
 
 template <int D>
 hipError_t scores_f32(const void* q_win, const void* k, int BH, int L, int W,
-                      const EvictLayout& lo, float scale2, char* ws, uint32_t* zero, int nzero,
+                      const EvictLayout& lo, float scale2, char* ws, uint32_t* zero, size_t nzero,
                       hipStream_t stream) {
   float2* stats = reinterpret_cast<float2*>(ws + lo.off_stats);
   float* lse = reinterpret_cast<float*>(ws + lo.off_lse);
@@ -599,7 +599,7 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
   // workspace) cleared by the log-sum-exp launch, which saves the top-k its clearing launch.
   const bool cleared = topk_multiblock(n, keep - W);
   uint32_t* hist = cleared ? reinterpret_cast<uint32_t*>(w + lo.off_topk) : nullptr;
-  const int nhist = cleared ? (int)topk_hist_words(BH) : 0;
+  const size_t nhist = cleared ? topk_hist_words(BH) : 0;
   hipError_t e;
   if (dtype == 0)
     e = D == 64 ? scores_f32<64>(q_win, k, BH, L, W, lo, scale2, w, hist, nhist, stream)
