@@ -483,7 +483,9 @@ __global__ __launch_bounds__(kThreads) void k_gather(const T* __restrict__ k,
   } else if (t >= nsel) {
     src = L - W + (t - nsel);
   } else {
-    src = kept[(size_t)bh * Lc + t];
+    // the kept-set top-k writes every slot below nsel with a prefix position; clamped all the
+    // same, so that no index read here can address outside the head's rows
+    src = min(max(kept[(size_t)bh * Lc + t], 0), L - W - 1);
   }
   if (li == 0 && (identity || t >= nsel)) kept[(size_t)bh * Lc + t] = src;
   if (k_out == nullptr) return;
