@@ -390,6 +390,24 @@ def test_fused_decode_step_rows_over_4096_pages(rkv):
         _check_fused_heads(rkv, w, q, k_c, v_c, topk, [(0, 0), (0, 1)], 0.125)
 
 
+def test_limits_at_their_maximum(rkv):
+    # the largest sizes the header accepts: a fused step over 8192 pages (16 per thread of the
+    # ranking block), and an fp32 eviction with G*W = 2048 window rows and the widest pooling
+    w = configs.SMALL[1].replace(name="p8192", B=1, Hq=4, Hkv=2, D=64, L=8192, keep=8192,
+                                 page_size=1, r=16, cfg_id=43)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    k_c = torch.randn((w.B, w.Hkv, w.Lc, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    v_c = torch.randn((w.B, w.Hkv, w.Lc, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn((w.B, w.Hq, w.D), device="cuda", generator=g).to(torch.bfloat16)
+    for topk in (1, 100, 8191, 8192):
+        _check_fused_heads(rkv, w, q, k_c, v_c, topk, [(0, 0), (0, 1)], 0.125)
+    we = configs.SMALL[2].replace(name="gw2048", dtype="fp32", B=1, Hq=16, Hkv=2, D=64,
+                                  L=700, W=256, keep=400, pool_kernel=127, cfg_id=44)
+    # a 127-wide box over a 444-token prefix smears the planted needles away: the oracle evicts
+    # them too, so only parity is checked here
+    _evict_check(rkv, we, gen.prompt_layer(we), needles=False)
+
+
 def _tied_keys(B, Hkv, P, ps, D, mode, seed):
     """K caches whose pages repeat, so that page scores tie exactly: every page the same, half
     of the pages the same, or pages in groups of three."""
