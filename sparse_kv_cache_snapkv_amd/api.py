@@ -48,6 +48,13 @@ def _dev(t: torch.Tensor, name: str, dtype: Optional[torch.dtype] = None) -> int
     return t.data_ptr()
 
 
+def _shape(t: Optional[torch.Tensor], name: str, shape: Tuple[int, ...]) -> None:
+    """The kernels index every buffer by the sizes the call passes, so a tensor of another shape
+    would be read or written past its end: refused here, before any pointer is handed over."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -96,6 +103,12 @@ def rkv_snapkvpp_evict(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ke
     dt = _dtype_code(k)
     Lc = min(keep, L)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _shape(k, "k", (B, Hkv, L, D))
+    _shape(v, "v", (B, Hkv, L, D))
+    _shape(kept_idx, "kept_idx", (B, Hkv, Lc))
+    _shape(k_out, "k_out", (B, Hkv, Lc, D))
+    _shape(v_out, "v_out", (B, Hkv, Lc, D))
+    _shape(pooled_out, "pooled_out", (B, Hkv, max(L - W, 1)))
     if kept_idx is None:
         kept_idx = torch.empty((B, Hkv, Lc), dtype=torch.int32, device=k.device)
     if not indices_only:
@@ -121,6 +134,8 @@ def rkv_build_page_summaries(k_c: torch.Tensor, page_size: int, *,
     """k_c [B,Hkv,Lc,D] -> (kmin_t, kmax_t) channel-major [B,Hkv,D,P]."""
     B, Hkv, Lc, D = k_c.shape
     P = -(-Lc // page_size)
+    _shape(kmin_t, "kmin_t", (B, Hkv, D, P))
+    _shape(kmax_t, "kmax_t", (B, Hkv, D, P))
     if kmin_t is None:
         kmin_t = torch.empty((B, Hkv, D, P), dtype=k_c.dtype, device=k_c.device)
     if kmax_t is None:
@@ -138,6 +153,10 @@ def rkv_hybrid_approx_scores(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torc
     """q [B,Hq,D]; summaries [B,Hkv,D,P] -> page_scores [B,Hkv,P] (and chan_idx [B,Hkv,r])."""
     B, Hq, D = q.shape
     Hkv, P = kmin_t.shape[1], kmin_t.shape[3]
+    _shape(kmin_t, "kmin_t", (B, Hkv, D, P))
+    _shape(kmax_t, "kmax_t", (B, Hkv, D, P))
+    _shape(page_scores, "page_scores", (B, Hkv, P))
+    _shape(chan_idx, "chan_idx", (B, Hkv, r))
     if page_scores is None:
         page_scores = torch.empty((B, Hkv, P), dtype=torch.float32, device=q.device)
     if return_channels and chan_idx is None:
@@ -156,6 +175,7 @@ def rkv_topk_select(scores: torch.Tensor, k: int, *, idx_out: Optional[torch.Ten
     n = scores.shape[-1]
     rows = scores.numel() // n
     kk = min(k, n)
+    _shape(idx_out, "idx_out", (*scores.shape[:-1], kk))
     if idx_out is None:
         idx_out = torch.empty((*scores.shape[:-1], kk), dtype=torch.int32, device=scores.device)
     nbytes = topk_workspace_bytes(rows, n, k)
@@ -175,6 +195,10 @@ def rkv_sparse_attend_decode(q: torch.Tensor, k_c: torch.Tensor, v_c: torch.Tens
     B, Hq, D = q.shape
     Hkv, Lc = k_c.shape[1], k_c.shape[2]
     n_pages = page_idx.shape[-1]
+    _shape(k_c, "k_c", (B, Hkv, Lc, D))
+    _shape(v_c, "v_c", (B, Hkv, Lc, D))
+    _shape(page_idx, "page_idx", (B, Hkv, n_pages))
+    _shape(out, "out", (B, Hq, D))
     dt = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
@@ -209,6 +233,18 @@ def decode_workspace_status(ws: torch.Tensor) -> int:
     return int(ws[:4].view(torch.int32).item())
 
 
+def _step_shapes(q, kmin_t, kmax_t, Hkv, P_rows, P, r, n_pages, chan_idx, page_scores,
+                 page_idx, out) -> None:
+    """Shapes of a fused step's summaries (P_rows pages per channel row) and outputs (P valid)."""
+    B, Hq, D = q.shape
+    _shape(kmin_t, "kmin_t", (B, Hkv, D, P_rows))
+    _shape(kmax_t, "kmax_t", (B, Hkv, D, P_rows))
+    _shape(chan_idx, "chan_idx", (B, Hkv, r))
+    _shape(page_scores, "page_scores", (B, Hkv, P))
+    _shape(page_idx, "page_idx", (B, Hkv, n_pages))
+    _shape(out, "out", (B, Hq, D))
+
+
 def rkv_hybrid_decode_step(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.Tensor,
                            k_c: torch.Tensor, v_c: torch.Tensor, page_size: int, r: int,
                            n_pages: int, scale: Optional[float] = None, *,
@@ -221,6 +257,10 @@ def rkv_hybrid_decode_step(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.
     [B,Hkv,Lc,D] -> out [B,Hq,D]. Optional outputs: chan_idx, page_scores, page_idx."""
     B, Hq, D = q.shape
     Hkv, Lc = k_c.shape[1], k_c.shape[2]
+    P = -(-Lc // page_size)
+    _shape(k_c, "k_c", (B, Hkv, Lc, D))
+    _shape(v_c, "v_c", (B, Hkv, Lc, D))
+    _step_shapes(q, kmin_t, kmax_t, Hkv, P, P, r, n_pages, chan_idx, page_scores, page_idx, out)
     dt = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
@@ -254,6 +294,8 @@ def rkv_build_page_summaries_cap(k_c: torch.Tensor, Lc: int, page_size: int, *,
     """k_c [B,Hkv,cap,D] (first Lc slots valid) -> (kmin_t, kmax_t) [B,Hkv,D,ceil(cap/ps)]."""
     B, Hkv, cap, D = k_c.shape
     pcap = -(-cap // page_size)
+    _shape(kmin_t, "kmin_t", (B, Hkv, D, pcap))
+    _shape(kmax_t, "kmax_t", (B, Hkv, D, pcap))
     if kmin_t is None:
         kmin_t = torch.empty((B, Hkv, D, pcap), dtype=k_c.dtype, device=k_c.device)
     if kmax_t is None:
@@ -270,7 +312,10 @@ def rkv_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_c: torch.Tensor, v
     """Writes k_new, v_new [B,Hkv,D] to slot Lc of k_c, v_c [B,Hkv,cap,D] and folds k_new into
     its page summary (kmin_t, kmax_t [B,Hkv,D,ceil(cap/ps)]). Returns the new length Lc + 1."""
     B, Hkv, cap, D = k_c.shape
-    _cap_shapes(k_c, kmin_t, page_size)
+    _, pcap = _cap_shapes(k_c, kmin_t, page_size)
+    _shape(v_c, "v_c", (B, Hkv, cap, D))
+    _shape(kmin_t, "kmin_t", (B, Hkv, D, pcap))
+    _shape(kmax_t, "kmax_t", (B, Hkv, D, pcap))
     if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
         raise ValueError("k_new, v_new must be [B, Hkv, D] of the caches")
     dt = k_c.dtype
@@ -294,7 +339,11 @@ def rkv_hybrid_decode_step_cap(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: to
     cap, page_size, n_pages)."""
     B, Hq, D = q.shape
     Hkv = k_c.shape[1]
-    cap, _ = _cap_shapes(k_c, kmin_t, page_size)
+    cap, pcap = _cap_shapes(k_c, kmin_t, page_size)
+    _shape(k_c, "k_c", (B, Hkv, cap, D))
+    _shape(v_c, "v_c", (B, Hkv, cap, D))
+    _step_shapes(q, kmin_t, kmax_t, Hkv, pcap, -(-Lc // page_size), r, n_pages, chan_idx,
+                 page_scores, page_idx, out)
     dt = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
@@ -340,6 +389,8 @@ def rkv_build_page_summaries_indexed(k: torch.Tensor, kept_idx: torch.Tensor, pa
     B, Hkv, L, D = k.shape
     Lc = _kept_rows(k, kept_idx)
     P = -(-Lc // page_size)
+    _shape(kmin_t, "kmin_t", (B, Hkv, D, P))
+    _shape(kmax_t, "kmax_t", (B, Hkv, D, P))
     if kmin_t is None:
         kmin_t = torch.empty((B, Hkv, D, P), dtype=k.dtype, device=k.device)
     if kmax_t is None:
@@ -364,6 +415,10 @@ def rkv_hybrid_decode_step_indexed(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t
     B, Hq, D = q.shape
     Hkv, L = k.shape[1], k.shape[2]
     Lc = _kept_rows(k, kept_idx)
+    P = -(-Lc // page_size)
+    _shape(k, "k", (B, Hkv, L, D))
+    _shape(v, "v", (B, Hkv, L, D))
+    _step_shapes(q, kmin_t, kmax_t, Hkv, P, P, r, n_pages, chan_idx, page_scores, page_idx, out)
     dt = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:

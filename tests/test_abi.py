@@ -176,3 +176,32 @@ def test_plan_budget_matches_the_oracle(lib):
     outs = [ctypes.c_int(-7) for _ in range(6)]
     assert lib.rkv_plan_budget(100, 64, 101, 10, *[ctypes.byref(o) for o in outs]) == -2
     assert all(o.value == -7 for o in outs)  # nothing written on error
+
+
+def test_binding_refuses_misshaped_buffers():
+    # the kernels index every buffer by the sizes a call passes: a tensor of another shape is
+    # refused before any pointer reaches the library (checked with host tensors: no GPU call)
+    import torch
+    import sparse_kv_cache_snapkv_amd as rkv
+    bf = torch.bfloat16
+    q = torch.zeros((1, 4, 64), dtype=bf)
+    k_c = torch.zeros((1, 2, 40, 64), dtype=bf)
+    kmin = torch.zeros((1, 2, 64, 10), dtype=bf)
+    with pytest.raises(ValueError, match="out"):
+        rkv.rkv_hybrid_decode_step(q, kmin, kmin, k_c, k_c, 4, 16, 4,
+                                   out=torch.zeros((1, 4, 32), dtype=bf))
+    with pytest.raises(ValueError, match="page_idx"):
+        rkv.rkv_hybrid_decode_step(q, kmin, kmin, k_c, k_c, 4, 16, 4,
+                                   page_idx=torch.zeros((1, 2, 3), dtype=torch.int32))
+    with pytest.raises(ValueError, match="kmin_t"):
+        rkv.rkv_hybrid_decode_step(q, kmin[..., :9], kmin, k_c, k_c, 4, 16, 4)
+    with pytest.raises(ValueError, match="page_scores"):
+        rkv.rkv_hybrid_approx_scores(q, kmin, kmin, 16, page_scores=torch.zeros((1, 2, 9)))
+    with pytest.raises(ValueError, match="idx_out"):
+        rkv.rkv_topk_select(torch.zeros((2, 100)), 5, idx_out=torch.zeros((2, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="kept_idx"):
+        rkv.rkv_snapkvpp_evict(torch.zeros((1, 4, 8, 64), dtype=bf), k_c, k_c, 16, 3,
+                               kept_idx=torch.zeros((1, 2, 15), dtype=torch.int32))
+    with pytest.raises(ValueError, match="v_c"):
+        rkv.rkv_sparse_attend_decode(q, k_c, k_c[:, :, :20].contiguous(),
+                                     torch.zeros((1, 2, 4), dtype=torch.int32), 4)
