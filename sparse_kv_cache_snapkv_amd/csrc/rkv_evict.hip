@@ -17,6 +17,8 @@
 // fp32 logits use plain FMAs (the small-workload path).
 #include <math.h>
 
+#include <algorithm>
+
 #include "rkv_common.hpp"
 #include "rkv_launch.hpp"
 
@@ -36,6 +38,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct EvictLayout {
   int GW, GWp, nchunk1, nsub1, nchunk2, nsub2, nprefix;
+  int mt1, parts1;  // bf16 passes: row tiles per block (4 or 8) and parts the window rows split into
+  int parts2;       // parts of the column sums (1 on the fp32 path, whose passes do not split)
   size_t off_stats, off_lse, off_colsum, off_pooled, off_topk, total;
 };
 
@@ -45,28 +49,32 @@ EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int keep, int dtype
   lo.GW = (Hq / Hkv) * W;
   lo.GWp = round32(lo.GW);
   lo.nprefix = L - W;
-  auto split = [&](int nkeys, int& nchunk, int& nsub) {
+  lo.mt1 = lo.GWp <= 128 ? 4 : 8;
+  lo.parts1 = (lo.GWp + 32 * lo.mt1 - 1) / (32 * lo.mt1);
+  lo.parts2 = dtype == 0 ? 1 : lo.parts1;
+  auto split = [&](int nkeys, int parts, int& nchunk, int& nsub) {
     const int subs = (nkeys + kKeysPerSub - 1) / kKeysPerSub;
-    int want = (kPassBlocks + BH - 1) / BH;
+    int want = (kPassBlocks + BH * parts - 1) / (BH * parts);
     if (want > subs) want = subs;
     if (want < 1) want = 1;
     nsub = (subs + want - 1) / want;
     nchunk = (subs + nsub - 1) / nsub;
     if (nchunk < 1) nchunk = 1;
   };
-  split(L, lo.nchunk1, lo.nsub1);
+  split(L, lo.parts1, lo.nchunk1, lo.nsub1);
   if (dtype == 0) {  // the fp32 pass 1 takes one 256-key chunk per block
     lo.nchunk1 = (L + kThreads - 1) / kThreads;
     lo.nsub1 = 1;
   }
-  split(lo.nprefix > 0 ? lo.nprefix : 1, lo.nchunk2, lo.nsub2);
+  split(lo.nprefix > 0 ? lo.nprefix : 1, lo.parts2, lo.nchunk2, lo.nsub2);
   size_t off = 0;
   lo.off_stats = off;
   off = align256(off + (size_t)BH * lo.nchunk1 * lo.GWp * sizeof(float2));
   lo.off_lse = off;
   off = align256(off + (size_t)BH * lo.GWp * sizeof(float));
   lo.off_colsum = off;
-  off = align256(off + (size_t)BH * (lo.nprefix > 0 ? lo.nprefix : 1) * sizeof(float));
+  off = align256(off + (size_t)lo.parts2 * BH * (lo.nprefix > 0 ? lo.nprefix : 1) *
+                           sizeof(float));
   lo.off_pooled = off;
   off = align256(off + (size_t)BH * (lo.nprefix > 0 ? lo.nprefix : 1) * sizeof(float));
   lo.off_topk = off;
@@ -118,8 +126,9 @@ __device__ __forceinline__ void stage_window_rows(uint16_t* smem, const bf16_t* 
 // Pass 1: per window row, the running (max, sum of exp2) of its scaled logits over this block's
 // keys, in log2 units. Each lane keeps the running pair of its row in every 32-row tile across
 // all of the block's key groups; the pairs of the lane halves and the four waves merge once at
-// the end. MT is the most 32-row tiles the kernel takes (GW <= 32 * MT): the running pairs of
-// every tile stay in registers.
+// the end. A block takes at most MT 32-row tiles (their running pairs stay in registers): the
+// window rows split into parts of 32 * MT rows, part p of chunk c being block x = p * nchunk + c,
+// so that the rows of a part fit two blocks per CU in LDS.
 template <int D, int MT>
 __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __restrict__ q_win,
                                                              const bf16_t* __restrict__ k, int L,
@@ -130,10 +139,13 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
   constexpr int QS = D + 8;
   constexpr int kMaxTiles = MT;
   extern __shared__ __align__(16) uint16_t smem[];
-  const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
+  const int GWp = (GW + 31) & ~31;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.y, chunk = blockIdx.x;
-  float2* wst = reinterpret_cast<float2*>(smem + (size_t)GWp * QS);  // [4][GWp]
+  const int bh = blockIdx.y, part = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+  const int row0 = part * 32 * MT;                 // this block's first window row
+  const int GWl = min(GW - row0, 32 * MT);         // and its row count
+  const int GWlp = (GWl + 31) & ~31, NRT = GWlp / 32;
+  float2* wst = reinterpret_cast<float2*>(smem + (size_t)GWlp * QS);  // [4][GWlp]
 
   // Key groups are interleaved over the chunks (group j of chunk c starts at key
   // (j * nchunk + c) * 256), so the blocks of a head sweep its keys as one front. Key registers
@@ -144,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
   bf16x8 kf0[2][KS], kf1[2][KS];
   load_key_tiles<D>(k_bh, key_of(0), L - 1, hf, n, kf0);
 
-  stage_window_rows<D>(smem, q_win + (size_t)bh * GW * D, GW, GWp, tid);
+  stage_window_rows<D>(smem, q_win + ((size_t)bh * GW + row0) * D, GWl, GWlp, tid);
   __syncthreads();
 
   float m[kMaxTiles], l[kMaxTiles];
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
       }
       // lane holds window row rt*32+n against keys key0 + kt*32 + 8*(i/4) + 4*hf + i%4
       if (masked) {
-        const int row = rt * 32 + n;
+        const int row = row0 + rt * 32 + n;               // the window row, in the whole group
         const int lim = row < GW ? L - W + (row % W) : -1;  // last visible key
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -218,28 +230,30 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
     const float mo = __shfl_xor(m[rt], 32, 64), lo = __shfl_xor(l[rt], 32, 64);
     const float mx = fmaxf(m[rt], mo);
     const float lx = mx == -INFINITY ? 0.f : l[rt] * exp2_hw(m[rt] - mx) + lo * exp2_hw(mo - mx);
-    if (hf == 0) wst[wave * GWp + rt * 32 + n] = make_float2(mx, lx);
+    if (hf == 0) wst[wave * GWlp + rt * 32 + n] = make_float2(mx, lx);
   }
   __syncthreads();
-  for (int r = tid; r < GW; r += kThreads) {
+  for (int r = tid; r < GWl; r += kThreads) {
     float mm = -INFINITY, ll = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float2 x = wst[w * GWp + r];
+      const float2 x = wst[w * GWlp + r];
       const float M = fmaxf(mm, x.x);
       if (M != -INFINITY) {
         ll = ll * exp2_hw(mm - M) + x.y * exp2_hw(x.x - M);
         mm = M;
       }
     }
-    stats[((size_t)bh * nchunk + chunk) * GWp + r] = make_float2(mm, ll);
+    stats[((size_t)bh * nchunk + chunk) * GWp + row0 + r] = make_float2(mm, ll);
   }
 }
 
 // Pass 2: for each prefix key, the sum over the group's window rows of exp2(scaled logit - row
 // log-sum-exp), i.e. its softmax probabilities summed over the G*W rows. Prefix keys are visible
-// to every row, so no mask is needed.
-template <int D>
+// to every row, so no mask is needed. The rows split into parts of 32 * MT as in pass 1 (block x
+// = p * nchunk + c); part p writes its partial sums to colsum + p * (rows of heads) * prefix, and
+// the pooling adds the parts in order.
+template <int D, int MT>
 __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __restrict__ q_win,
                                                               const bf16_t* __restrict__ k,
                                                               const float* __restrict__ lse,
@@ -249,11 +263,14 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
   constexpr int KS = D / 16;
   constexpr int QS = D + 8;
   extern __shared__ __align__(16) uint16_t smem[];
-  const int GWp = (GW + 31) & ~31, NRT = GWp / 32;
+  const int GWp = (GW + 31) & ~31;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int bh = blockIdx.y, part = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+  const int row0 = part * 32 * MT, GWl = min(GW - row0, 32 * MT);
+  const int GWlp = (GWl + 31) & ~31, NRT = GWlp / 32;
   const int nprefix = L - W;
-  float* s_lse = reinterpret_cast<float*>(smem + (size_t)GWp * QS);
+  float* s_lse = reinterpret_cast<float*>(smem + (size_t)GWlp * QS);
+  float* csp = colsum + (size_t)part * gridDim.y * nprefix;  // this part's partial sums
 
   // Key groups interleaved over the chunks and double-buffered as in pass 1, but visited in the
   // reverse of pass 1's order: the groups pass 1 read last are the likeliest to still be held by
@@ -264,10 +281,10 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
   bf16x8 kf0[2][KS], kf1[2][KS];
   load_key_tiles<D>(k_bh, key_of(0), nprefix - 1, hf, n, kf0);
 
-  stage_window_rows<D>(smem, q_win + (size_t)bh * GW * D, GW, GWp, tid);
-  for (int r = tid; r < GWp; r += kThreads) {
-    const float x = lse[(size_t)bh * GWp + min(r, GW - 1)];
-    s_lse[r] = r < GW ? x : INFINITY;  // padded rows add exp2(-inf) = 0
+  stage_window_rows<D>(smem, q_win + ((size_t)bh * GW + row0) * D, GWl, GWlp, tid);
+  for (int r = tid; r < GWlp; r += kThreads) {
+    const float x = lse[(size_t)bh * GWp + row0 + min(r, GWl - 1)];
+    s_lse[r] = r < GWl ? x : INFINITY;  // padded rows add exp2(-inf) = 0
   }
   __syncthreads();
 
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
     for (int kt = 0; kt < 2; ++kt) {
       const float tot = cs[kt] + __shfl_xor(cs[kt], 32, 64);
       const int key = key0 + kt * 32 + n;
-      if (hf == 0 && key < nprefix) colsum[(size_t)bh * nprefix + key] = tot;
+      if (hf == 0 && key < nprefix) csp[(size_t)bh * nprefix + key] = tot;
     }
   };
   for (int t = 0; t < nsub; t += 2) {  // the next group's loads always go out, as in pass 1
@@ -432,15 +449,19 @@ __global__ __launch_bounds__(kThreads) void k_win_lse(const float2* __restrict__
 // its halo are staged in LDS.
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void k_pool(const float* __restrict__ colsum, int n,
-                                                   int kernel, float* __restrict__ pooled) {
+                                                   int parts, int kernel,
+                                                   float* __restrict__ pooled) {
   __shared__ float tile[kThreads + 128];
   const int bh = blockIdx.y;
   const int h = kernel / 2;
   const int j0 = blockIdx.x * kThreads;
   const float* src = colsum + (size_t)bh * n;
+  const size_t pstride = (size_t)gridDim.y * n;  // between the window-row parts' partial sums
   for (int i = threadIdx.x; i < kThreads + 2 * h; i += kThreads) {
     const int j = j0 - h + i;
-    const float x = src[min(max(j, 0), n - 1)];  // every address inside the row
+    const int jc = min(max(j, 0), n - 1);  // every address inside the row
+    float x = src[jc];
+    for (int p = 1; p < parts; ++p) x += src[p * pstride + jc];
     tile[i] = (j >= 0 && j < n) ? x : 0.f;
   }
   __syncthreads();
@@ -523,27 +544,30 @@ hipError_t scores_bf16(const void* q_win, const void* k, int BH, int L, int W,
   float2* stats = reinterpret_cast<float2*>(ws + lo.off_stats);
   float* lse = reinterpret_cast<float*>(ws + lo.off_lse);
   float* colsum = reinterpret_cast<float*>(ws + lo.off_colsum);
-  const size_t lds1 = (size_t)lo.GWp * QS * 2 + (size_t)lo.GWp * sizeof(float2) * 4;
-  const size_t lds2 = (size_t)lo.GWp * QS * 2 + (size_t)lo.GWp * sizeof(float);
+  const int rows = std::min(lo.GWp, 32 * MT);  // window rows per block of either pass
+  const size_t lds1 = (size_t)rows * QS * 2 + (size_t)rows * sizeof(float2) * 4;
+  const size_t lds2 = (size_t)rows * QS * 2 + (size_t)rows * sizeof(float);
   hipError_t e = hipSuccess;
   if (lds1 > 64 * 1024 &&
       (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_stats_mfma<D, MT>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1)) != hipSuccess)
     return e;
   if (lds2 > 64 * 1024 &&
-      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_colsum_mfma<D>),
+      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_win_colsum_mfma<D, MT>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL((k_win_stats_mfma<D, MT>), dim3(lo.nchunk1, BH), dim3(kThreads), lds1, stream,
-                     static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), L, W, lo.GW,
-                     lo.nsub1, lo.nchunk1, scale2, stats);
+  hipLaunchKernelGGL((k_win_stats_mfma<D, MT>), dim3(lo.nchunk1 * lo.parts1, BH), dim3(kThreads),
+                     lds1, stream, static_cast<const bf16_t*>(q_win),
+                     static_cast<const bf16_t*>(k), L, W, lo.GW, lo.nsub1, lo.nchunk1, scale2,
+                     stats);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_win_lse, dim3((lo.GW + 3) / 4, BH), dim3(kThreads), 0, stream, stats,
                      lo.nchunk1, lo.GW, lse, zero, nzero);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_win_colsum_mfma<D>, dim3(lo.nchunk2, BH), dim3(kThreads), lds2, stream,
-                     static_cast<const bf16_t*>(q_win), static_cast<const bf16_t*>(k), lse, L, W,
-                     lo.GW, lo.nsub2, lo.nchunk2, scale2, colsum);
+  hipLaunchKernelGGL((k_win_colsum_mfma<D, MT>), dim3(lo.nchunk2 * lo.parts2, BH),
+                     dim3(kThreads), lds2, stream, static_cast<const bf16_t*>(q_win),
+                     static_cast<const bf16_t*>(k), lse, L, W, lo.GW, lo.nsub2, lo.nchunk2, scale2,
+                     colsum);
   return hipGetLastError();
 }
 
@@ -551,9 +575,9 @@ template <int D>
 hipError_t scores_bf16_any(const void* q_win, const void* k, int BH, int L, int W,
                            const EvictLayout& lo, float scale2, char* ws, uint32_t* zero,
                            size_t nzero, hipStream_t stream) {
-  return lo.GWp <= 128
+  return lo.mt1 == 4
              ? scores_bf16<D, 4>(q_win, k, BH, L, W, lo, scale2, ws, zero, nzero, stream)
-             : scores_bf16<D, 16>(q_win, k, BH, L, W, lo, scale2, ws, zero, nzero, stream);
+             : scores_bf16<D, 8>(q_win, k, BH, L, W, lo, scale2, ws, zero, nzero, stream);
 }
 
 template <int D>
@@ -614,10 +638,10 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
   float* pooled = pooled_out != nullptr ? pooled_out : reinterpret_cast<float*>(w + lo.off_pooled);
   if (pool_type == 0)
     hipLaunchKernelGGL(k_pool<0>, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0,
-                       stream, colsum, n, pool_kernel, pooled);
+                       stream, colsum, n, lo.parts2, pool_kernel, pooled);
   else
     hipLaunchKernelGGL(k_pool<1>, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0,
-                       stream, colsum, n, pool_kernel, pooled);
+                       stream, colsum, n, lo.parts2, pool_kernel, pooled);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   e = cleared ? launch_topk_cleared(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk,
                                     stream)
