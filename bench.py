@@ -110,6 +110,50 @@ def algorithmic_bytes(w, topk: int) -> dict:
                 evict=evict)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def evict_70b_layer(rkv, torch, reps: int = 3) -> dict:
+    """SnapKV++ eviction of one layer of the 70B-shaped workload (64/8 heads, D 128, context
+    262144, window 64, keep 32768): the shape where the window passes are bound by MFMA and the
+    exponentials rather than by HBM. Default stream, inputs resident, events around `reps`
+    calls after one warm-up call."""
+    from workloads import configs, generate as gen
+    w = configs.LLAMA70B_256K_80L
+    dev = torch.device("cuda:0")
+    p = gen.device_prompt_layer(w, 0, dev)
+    B, Hq, Hkv, D, L, W, keep = w.B, w.Hq, w.Hkv, w.D, w.L, w.W, w.keep
+    kept = torch.empty((B, Hkv, keep), dtype=torch.int32, device=dev)
+    kc = torch.empty((B, Hkv, keep, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    ws = torch.empty(rkv.snapkvpp_workspace_bytes(B, Hq, Hkv, L, D, W, keep, 1),
+                     dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D)
+
+    def run():
+        rkv.rkv_snapkvpp_evict(p["q_win"], p["k"], p["v"], keep, w.pool_kernel, "avg", scale,
+                               kept_idx=kept, k_out=kc, v_out=vc, workspace=ws)
+
+    torch.cuda.synchronize()
+    run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    flops = 4 * B * Hq * W * L * D  # the two window passes' QK^T
+    nb = (B * Hkv * L * D * 2 + B * Hq * W * D * 2 + 4 * B * Hkv * keep * D * 2
+          + B * Hkv * keep * 4)
+    del p, kept, kc, vc, ws
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, us_per_layer=round(us, 1), mfma_flops=flops,
+                mfma_TFLOPs=round(flops / (us * 1e-6) / 1e12, 1),
+                mfma_frac=round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                algorithmic_bytes=nb, GBps=round(nb / (us * 1e-6) / 1e9, 1))
+
+
 def cpu_baseline(w, sample_steps: int):
     """The oracle, as it stands, on one KV head of the workload; scaled to us per decode step."""
     import numpy as np
@@ -391,6 +435,9 @@ def main() -> int:
                    append_bytes=app_bytes, append_plus_step_us=round(grow_us["append+step"], 3),
                    step_topk=tk_g, sync_status=rkv.decode_workspace_status(ws_g))
 
+    # ---- outside the timed region: one layer of the 70B-shaped workload's eviction
+    evict_70b = evict_70b_layer(rkv, torch)
+
     per_topk = {}
     stages_out = {}
     split_us = {name: ms * 1e3 / nsteps for name, ms in stage_ms.items() if name.startswith("split_")}
@@ -441,7 +488,8 @@ def main() -> int:
                     context=w.L, window=w.W, pool_kernel=w.pool_kernel, keep=w.keep,
                     page_size=w.page_size, channels=w.r, topk=list(w.topk),
                     decode_steps=nsteps, replicas=R),
-        per_topk=per_topk, stages=stages, growing_cache=growing, selection_quality=sel_q,
+        per_topk=per_topk, stages=stages, evict_70b_layer=evict_70b, growing_cache=growing,
+        selection_quality=sel_q,
         roofline=roofline,
         sync_status=status,
         wall_ms_timed=round(wall_ms, 1))
