@@ -1,10 +1,11 @@
 """Selection quality of the hybrid approximation against Exact-TopK, from the library's calls.
 
-RocketKV rebuttal, "Measurement of Exact-TopK": an oracle-based method that knows token
-importance and picks the top tokens for each attention head and decoding step. "Novelty: RocketKV
-is SnapKV + QUEST": at one compression ratio, splitting it over the sequence and the head
-dimensions loses less than compressing the sequence alone (QUEST) or the head dimension alone
-(SparQ). These metrics measure that axis on synthetic data, with no dataset.
+Exact-TopK (rebuttal, "Measurement of Exact-TopK") is the reference selection that ranks tokens by
+their true scores, separately per query head and per step. Its recall and the share of the exact
+softmax mass that a selection covers are the two measures used here. "Novelty: RocketKV is
+SnapKV + QUEST" argues that one compression ratio is better spent on both the sequence and the
+head dimension than on either alone (QUEST-like: whole-channel pages; SparQ-like: one-token
+pages); the same measures compare those settings on synthetic data, with no dataset.
 
 The heavy work runs in librkv. Exact per-head scores are the approximate scores of one-token
 pages over all D channels, on a copy of K per query head: for one-token pages Kmin = Kmax = K, and

@@ -482,3 +482,54 @@ def test_selection_quality_exact_topk_maximises_mass_by_brute_force():
     coarse = O.selection_quality(q, k, 4, 1, topk + 1, 0.7)
     assert 0.0 <= coarse["recall"] <= 1.0 and coarse["mass"] <= 1.0 + 1e-12
     assert O.selection_quality(q, k, 2, D, Lc, 0.7)["mass"] > 1 - 1e-12  # every token selected
+
+
+def test_selection_quality_hand_computed_mass_and_recall():
+    # Worked by hand (rebuttal, "Measurement of Exact-TopK": the best tokens of each head and
+    # step; "Explanation of Calculating Approximate Attention Scores": channels by the group sum
+    # of |q|, bound from the group sum of q). D = 2, one KV head, one-token pages, one channel,
+    # top-1, scale = ln 2 so that every softmax weight is a power of two.
+    #   keys k0 = (1, 0), k1 = (0, 3), k2 = (0, 0), k3 = (-1, 0)
+    # Case G = 1, q = (2, 1): |q| picks channel 0, qbar_0 = 2 > 0 reads the page maxima (the keys
+    # themselves), so the bound is (2, 0, 0, -2) and the hybrid keeps k0. Exact scores are
+    # (2, 3, 0, -2): Exact-TopK keeps k1, recall 0. Weights 2^s = (4, 8, 1, 1/4), total 53/4:
+    # mass = 4 / (53/4) = 16/53, mass_exact = 32/53.
+    k = np.array([[[[1.0, 0.0], [0.0, 3.0], [0.0, 0.0], [-1.0, 0.0]]]])
+    q1 = np.array([[[2.0, 1.0]]])
+    res = O.selection_quality(q1, k, 1, 1, 1, math.log(2.0))
+    assert res["recall"] == 0.0
+    assert math.isclose(res["mass"], 16 / 53, rel_tol=1e-12)
+    assert math.isclose(res["mass_exact"], 32 / 53, rel_tol=1e-12)
+    # Case G = 2, heads q0 = (2, 1), q1 = (1, -3): sum |q| = (3, 4) picks channel 1 with
+    # qbar_1 = -2 < 0, which reads the page minima: bound (0, -6, 0, 0); the tie at 0 goes to the
+    # lowest page, so the hybrid keeps k0 for both heads.
+    #   head 0: as above, recall 0, mass 16/53, mass_exact 32/53.
+    #   head 1: exact scores (1, -9, 0, -1), Exact-TopK keeps k0 (recall 1); weights
+    #   (2, 2^-9, 1, 1/2), total 1793/512, so mass = mass_exact = 1024/1793.
+    # Means over the two heads: recall 1/2, mass (16/53 + 1024/1793)/2,
+    # mass_exact (32/53 + 1024/1793)/2.
+    q2 = np.array([[[2.0, 1.0], [1.0, -3.0]]])
+    res = O.selection_quality(q2, k, 1, 1, 1, math.log(2.0))
+    assert res["recall"] == 0.5
+    assert math.isclose(res["mass"], (16 / 53 + 1024 / 1793) / 2, rel_tol=1e-12)
+    assert math.isclose(res["mass_exact"], (32 / 53 + 1024 / 1793) / 2, rel_tol=1e-12)
+    # a dropped or doubled scale moves the mass off the hand-computed value
+    for wrong in (1.0, 2 * math.log(2.0)):
+        assert not math.isclose(O.selection_quality(q1, k, 1, 1, 1, wrong)["mass"], 16 / 53,
+                                rel_tol=1e-3)
+
+
+@pytest.mark.parametrize("L,kernel", [(2048, 7), (32768, 31), (131072, 63), (262144, 63)])
+def test_plan_budget_pooling_kernel_at_the_configured_lengths(L, kernel):
+    # The pages give only the trend of the pooling kernel with input length ("Potential
+    # Sensitivity to Kernel Size in SnapKV++": longer inputs, larger kernels). The four evaluated
+    # workloads pair these context lengths with these kernels (2K: 7, 32K: 31, 128K and 256K: 63),
+    # and the planner's table must reproduce them.
+    assert O.plan_budget(L, 128, 32, 256)["pool_kernel"] == kernel
+
+
+def test_plan_budget_pooling_kernel_grows_with_length():
+    lengths = [64, 2048, 4096, 4097, 16384, 16385, 65536, 65537, 131072, 1 << 20]
+    ks = [O.plan_budget(L, 128, 32, 64)["pool_kernel"] for L in lengths]
+    assert ks == sorted(ks) and all(k % 2 == 1 for k in ks)
+    assert ks[0] == 7 and ks[-1] == 63
