@@ -10,9 +10,10 @@
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers to dense row-major arrays unless stated otherwise. The caller
- *     owns every buffer, workspaces included; the library never allocates, frees or synchronises
- *     and keeps no state between calls, so concurrent calls on different streams are safe as
- *     long as their output and workspace buffers do not overlap.
+ *     owns every buffer, workspaces included; the library never allocates or frees, and it
+ *     synchronises only in rkv_hybrid_decode_status. It keeps no state between calls apart from
+ *     what a workspace holds, so concurrent calls on different streams are safe as long as their
+ *     output and workspace buffers do not overlap.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously.
  *   - dtype: RKV_F32 (float) or RKV_BF16 (bfloat16 stored as uint16 bit patterns). q, K, V,
  *     summaries and attention outputs share the call's dtype; scores, pooled scores and all
@@ -206,13 +207,18 @@ int rkv_sparse_attend_decode(const void* q, const void* k_c, const void* v_c,
  * ws          rkv_hybrid_decode_workspace_bytes(...) bytes (its size depends on the shape B,
  *             Hq, Hkv, Lc, D, page_size and dtype, not on n_pages), zero-filled ONCE by
  *             rkv_hybrid_decode_workspace_init before its first use, and again before it is used
- *             for a different shape. The blocks of a head exchange scores and partial results
- *             through it as 64-bit words tagged with a per-head call counter that the workspace
- *             also holds, so no call has to clear anything for the next one; readers wait for
- *             current tags with a bounded wait, and the grid never exceeds one block per CU. If
- *             a wait ever gave up (only possible when other work occupies the GPU's CUs at the
- *             same time), the uint32 at byte offset 0 of ws becomes nonzero and stays so: that
- *             call's output is not valid. Calls that overlap in time must not share a workspace.
+ *             for a different shape. The workspace holds, per KV head, a call counter and two
+ *             ticket counters. The blocks of a head take their roles in the order they start (a
+ *             ticket), exchange scores and partial results through the workspace as 64-bit words
+ *             tagged with the call counter, and wait only for blocks that started before them; so
+ *             a call finishes however its blocks are scheduled, also while other work shares the
+ *             GPU, and the block that finishes a head leaves its counters ready for the next call
+ *             (no call has to clear anything). Each wait is bounded by about 1 ms of wall-clock
+ *             time; a wait that runs out (a block stalled far beyond the step's own duration)
+ *             sets a bit of the workspace's status word and the call's output is not valid: read
+ *             it with rkv_hybrid_decode_status, and initialise the workspace again before reusing
+ *             it. Calls that overlap in time must not share a workspace; calls on different
+ *             workspaces may run concurrently on any streams.
  * ------------------------------------------------------------------------------------------ */
 int rkv_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size,
                                       int n_pages, int dtype, size_t* bytes);
@@ -222,6 +228,14 @@ int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t
                            int D, int page_size, int r, int n_pages, float scale, int dtype,
                            int32_t* chan_idx, float* page_scores, int32_t* page_idx, void* out,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* The fused step's status word: *status (host memory) receives the bits set by calls on this
+ * workspace since it was initialised or last cleared: 1 = a wait for page scores ran out of time,
+ * 2 = a wait for attention partials ran out of time, 4 = a block drew a ticket beyond its call's
+ * plan (counters left inconsistent by an earlier failed call). 0 means every call's output is
+ * valid. clear != 0 zeroes the word after reading it. The read is enqueued on `stream` after the
+ * work already there, and this call SYNCHRONISES the stream before returning. */
+int rkv_hybrid_decode_status(void* ws, size_t ws_bytes, int clear, uint32_t* status, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Decode-time append into a compressed cache that grows ([rebuttal] "SCBench Results": plain

@@ -27,6 +27,8 @@ SIGNATURES = {
                                  + [_vp, _vp, _c_size, _vp]),
     "rkv_hybrid_decode_workspace_bytes": (_c_int, [_c_int] * 8 + [_szp]),
     "rkv_hybrid_decode_workspace_init": (_c_int, [_vp, _c_size, _vp]),
+    "rkv_hybrid_decode_status": (_c_int, [_vp, _c_size, _c_int, ctypes.POINTER(ctypes.c_uint32),
+                                          _vp]),
     "rkv_hybrid_decode_step": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int]
                                + [_vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "rkv_build_page_summaries_cap": (_c_int, [_vp] + [_c_int] * 7 + [_vp, _vp, _vp]),

@@ -228,9 +228,14 @@ def rkv_hybrid_decode_workspace(q: torch.Tensor, Hkv: int, Lc: int, page_size: i
     return ws
 
 
-def decode_workspace_status(ws: torch.Tensor) -> int:
-    """The workspace status word (nonzero: a fused step's cross-block wait gave up)."""
-    return int(ws[:4].view(torch.int32).item())
+def decode_workspace_status(ws: torch.Tensor, clear: bool = False) -> int:
+    """The fused step's status word through rkv_hybrid_decode_status (synchronises the current
+    stream): 0 when every call on this workspace was valid, else its failure bits."""
+    val = ctypes.c_uint32(0)
+    _check("rkv_hybrid_decode_status", _lib.load().rkv_hybrid_decode_status(
+        ws.data_ptr(), ws.numel() * ws.element_size(), int(bool(clear)), ctypes.byref(val),
+        _stream(ws)))
+    return int(val.value)
 
 
 def _step_shapes(q, kmin_t, kmax_t, Hkv, P_rows, P, r, n_pages, chan_idx, page_scores,

@@ -273,6 +273,13 @@ int rkv_hybrid_decode_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return launch_status(rkv::launch_decode_ws_init(ws, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
+int rkv_hybrid_decode_status(void* ws, size_t ws_bytes, int clear, uint32_t* status,
+                             void* stream) {
+  if (!ws || !status) return RKV_ERR_NULL;
+  if (ws_bytes < 256 || !aligned16(ws)) return RKV_ERR_WORKSPACE;
+  return launch_status(rkv::read_decode_status(ws, clear, status, static_cast<hipStream_t>(stream)));
+}
+
 int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
                            const void* k_c, const void* v_c, int B, int Hq, int Hkv, int Lc,
                            int D, int page_size, int r, int n_pages, float scale, int dtype,

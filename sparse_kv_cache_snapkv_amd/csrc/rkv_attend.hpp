@@ -1,0 +1,224 @@
+// Exact softmax attention over the tokens of selected pages, shared by the G query heads of a GQA
+// group (RocketKV rebuttal, "Lack of Direct Latency Comparison": Step 3 sparse attention;
+// "Explanation of Calculating Approximate Attention Scores": one selection per group). The
+// per-wave state below is used by the standalone attention call and by the fused decode step.
+//
+// A token row of D elements is spread over LPT lanes, 16 bytes each, so one load instruction
+// fetches TPL = 64/LPT whole rows; per chunk a wave issues all its K and V loads (SLOTS of each)
+// before reducing in registers (DPP inside a row of 16 lanes), with an online softmax across
+// chunks. The waves of a block merge (max, sum, P.V) through LDS.
+#pragma once
+
+#include <math.h>
+
+#include "rkv_common.hpp"
+
+namespace rkv {
+
+constexpr int kAttThreads = 256;
+constexpr int kAttWaves = kAttThreads / kWave;
+constexpr int kAttSlots = 4;            // row loads per wave per chunk (standalone attention)
+constexpr int kMaxPagesPerSplit = 1024;
+
+template <typename T, int D, int SLOTS = kAttSlots>
+struct Geo {
+  static constexpr int V = vec16<T>::n;
+  static constexpr int LPT = D / V;
+  static constexpr int TPL = kWave / LPT;
+  static constexpr int WTOK = SLOTS * TPL;  // tokens per wave per chunk
+};
+
+template <int D, int G, int NW = kAttWaves>
+struct AttendShared {
+  int pages[kMaxPagesPerSplit + kWave];  // slots from kMaxPagesPerSplit: discarded writes, per lane
+  float m[NW][G], l[NW][G];
+  float o[NW][G][D];
+};
+
+// Per-wave online-softmax state of the G heads of a group; NW waves share a block's page list and
+// each issues SLOTS K and V row loads per chunk. bf16 scores are packed bf16 dot products of the
+// raw query and key bits, scaled after the lane reduction; fp32 scores use the pre-scaled query.
+template <typename T, int D, int G, int NW = kAttWaves, int SLOTS = kAttSlots>
+struct WaveState {
+  static constexpr bool kBf16 = elem<T>::bytes == 2;
+  float qf[G][Geo<T, D, SLOTS>::V];  // fp32 only: the query times scale * log2(e)
+  float m[G], l[G], acc[G][Geo<T, D, SLOTS>::V];
+  uint4 qraw[G];
+  float sc2;     // scale * log2(e)
+  bool started;  // a chunk has been accumulated (before it, rescaling zeros is skipped)
+
+  // The lane's slices of the G queries, as loaded; init(scale2) converts them.
+  __device__ __forceinline__ void load_q(const T* __restrict__ q_bh) {
+    constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT;
+    const int li = (threadIdx.x & (kWave - 1)) % LPT;
+#pragma unroll
+    for (int g = 0; g < G; ++g) qraw[g] = load16(q_bh + (size_t)g * D + li * V);
+  }
+
+  __device__ __forceinline__ void init(const T* __restrict__ q_bh, float scale2) {
+    load_q(q_bh);
+    init(scale2);
+  }
+
+  __device__ __forceinline__ void init(float scale2) {
+    constexpr int V = Geo<T, D, SLOTS>::V;
+    sc2 = scale2;
+    started = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if constexpr (!kBf16) {
+        unpack16<T>(qraw[g], qf[g]);
+#pragma unroll
+        for (int e = 0; e < V; ++e) qf[g][e] *= scale2;
+      }
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[g][e] = 0.f;
+    }
+  }
+
+  // Tokens [0, ntok) of the page list `pages` (LDS): this wave takes chunks wave, wave+4, ...
+  // rows (may be null): slot t of the compressed view is row rows[t] of kc_bh / vc_bh, clamped
+  // into [0, row_hi] (the multi-turn variant keeps the whole cache and indexes its kept rows).
+  __device__ __forceinline__ void run(const T* __restrict__ kc_bh, const T* __restrict__ vc_bh,
+                                      const int* pages, int ntok, int ps, int P, int Lc,
+                                      const int32_t* __restrict__ rows = nullptr,
+                                      int row_hi = 0) {
+    constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT, TPL = Geo<T, D, SLOTS>::TPL;
+    constexpr int WTOK = Geo<T, D, SLOTS>::WTOK;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lg = lane / LPT, li = lane % LPT;
+    const T* kb = kc_bh + li * V;
+    const T* vb = vc_bh + li * V;
+    for (int c0 = wave * WTOK; c0 < ntok; c0 += NW * WTOK) {
+      int tok[SLOTS];
+      bool ok[SLOTS];
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const int ti = c0 + s * TPL + lg;
+        bool valid = ti < ntok;
+        const int page = valid ? pages[ti / ps] : 0;
+        const int t = page * ps + ti % ps;
+        valid = valid && page >= 0 && page < P && t < Lc;
+        ok[s] = valid;
+        tok[s] = valid ? t : 0;
+      }
+      if (rows != nullptr) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) tok[s] = min(max(rows[tok[s]], 0), row_hi);
+      }
+      uint4 kr[SLOTS], vr[SLOTS];
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        kr[s] = load16_stream(kb + (size_t)tok[s] * D);
+        vr[s] = load16_stream(vb + (size_t)tok[s] * D);
+      }
+      float sc[SLOTS][G];
+      if constexpr (kBf16) {
+        float d[SLOTS * G];
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+          for (int g = 0; g < G; ++g) d[s * G + g] = dot8_bf16(qraw[g], kr[s]);
+        group_sum_n<LPT>(d);
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+          for (int g = 0; g < G; ++g) sc[s][g] = ok[s] ? d[s * G + g] * sc2 : -INFINITY;
+      } else {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+          float kf[V];
+          unpack16<T>(kr[s], kf);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) d = fmaf(qf[g][e], kf[e], d);
+            d = group_sum<LPT>(d);
+            sc[s][g] = ok[s] ? d : -INFINITY;
+          }
+        }
+      }
+      float mu[G], f[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float x = sc[0][g];
+#pragma unroll
+        for (int s = 1; s < SLOTS; ++s) x = fmaxf(x, sc[s][g]);
+        x = across_max<LPT>(x);
+        const float mn = fmaxf(m[g], x);
+        f[g] = mn == -INFINITY ? 1.f : exp2_hw(m[g] - mn);
+        mu[g] = mn == -INFINITY ? 0.f : mn;
+        m[g] = mn;
+      }
+      // `started` is the same in every lane; until the first chunk, l and acc are zero
+      if (__builtin_amdgcn_readfirstlane((int)started)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          l[g] *= f[g];
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[g][e] *= f[g];
+        }
+      }
+      started = true;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        float vf[V];
+        unpack16<T>(vr[s], vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = exp2_hw(sc[s][g] - mu[g]);
+          l[g] += p;
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+        }
+      }
+    }
+  }
+
+  // Reduces over the wave's lane groups and stores (m, l, o) of this wave in sh.
+  __device__ __forceinline__ void publish(AttendShared<D, G, NW>& sh) {
+    constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lg = lane / LPT, li = lane % LPT;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      l[g] = across_sum<LPT>(l[g]);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[g][e] = across_sum<LPT>(acc[g][e]);
+    }
+    if (lg == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) sh.o[wave][g][li * V + e] = acc[g][e];
+        if (li == 0) {
+          sh.m[wave][g] = m[g];
+          sh.l[wave][g] = l[g];
+        }
+      }
+    }
+  }
+};
+
+// Combines the NW waves' (m, l, o) for output element idx = g*D + c.
+template <int D, int G, int NW = kAttWaves>
+__device__ __forceinline__ void wave_merge(const AttendShared<D, G, NW>& sh, int g, int c, float& M,
+                                           float& lsum, float& o) {
+  M = sh.m[0][g];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sh.m[w][g]);
+  lsum = 0.f;
+  o = 0.f;
+  if (M == -INFINITY) return;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float fw = exp2_hw(sh.m[w][g] - M);
+    lsum = fmaf(sh.l[w][g], fw, lsum);
+    o = fmaf(sh.o[w][g][c], fw, o);
+  }
+}
+
+}  // namespace rkv

@@ -7,6 +7,9 @@
 
 namespace rkv {
 
+// Compute units of the current device (at most 256), cached per device.
+int device_cus();
+
 // Element-wise page min/max of the first Lc slots of k_c [BH, kv_pitch, D] into channel-major
 // [BH, D, ceil(cap/page_size)] (its first ceil(Lc/page_size) pages). rows (may be null): slot t
 // of head bh is row rows[bh*Lc + t] of k_c.
@@ -45,10 +48,14 @@ hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
                                 void* ws, hipStream_t stream);
 
 // One fused decode step in a single kernel: approximate page scores, page top-k, attention and
-// split merge; the blocks of a head synchronise through counters in the workspace.
+// split merge; the blocks of a head draw their roles from ticket counters in the workspace and
+// exchange tagged words through it.
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int n_pages,
                        int dtype);
 hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream);
+// Copies the workspace's status word to *status (host memory), optionally clears it, and
+// synchronises the stream.
+hipError_t read_decode_status(void* ws, int clear, uint32_t* status, hipStream_t stream);
 // Caches of kv_pitch rows per head (slot t is row t, or rows[bh*Lc + t] when rows is given),
 // summaries of ceil(cap/page_size) pages per channel row (the first ceil(Lc/page_size) valid);
 // the workspace is laid out for cap.

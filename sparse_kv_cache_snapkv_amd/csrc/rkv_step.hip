@@ -1,0 +1,116 @@
+// Host side of the fused decode step (rkv_step.hpp): plan, workspace layout, launch, and the
+// workspace's initialisation and status word.
+#include <algorithm>
+
+#include "rkv_launch.hpp"
+#include "rkv_step.hpp"
+
+namespace rkv {
+
+namespace {
+
+constexpr int kWaitMicroseconds = 1000;  // bound of one cross-block wait
+
+__global__ void k_zero_u32(unsigned* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// Steady-counter ticks per wait bound on the current device (the counter's rate is a device
+// attribute, in kHz).
+long long wait_ticks() {
+  static long long cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz < 1)
+      khz = 100000;  // 100 MHz
+    cache[dev] = (long long)khz * kWaitMicroseconds / 1000;
+  }
+  return cache[dev];
+}
+
+}  // namespace
+
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int, int) {
+  const int P = (Lc + page_size - 1) / page_size;
+  return step::layout(B, Hq, Hkv, D, P).total;
+}
+
+hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / sizeof(unsigned);
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_zero_u32, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream,
+                     static_cast<unsigned*>(ws), n);
+  return hipGetLastError();
+}
+
+hipError_t read_decode_status(void* ws, int clear, uint32_t* status, hipStream_t stream) {
+  hipError_t e = hipMemcpyAsync(status, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return e;
+  if (clear) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, stream, static_cast<unsigned*>(ws),
+                       (size_t)1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipStreamSynchronize(stream);
+}
+
+hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kmax_t,
+                              const void* k_c, const void* v_c, const int32_t* rows, int B, int Hq,
+                              int Hkv, int Lc, int kv_pitch, int cap, int D, int page_size, int r,
+                              int n_pages, float scale, int dtype, int32_t* chan_idx,
+                              float* page_scores, int32_t* page_idx, void* out, void* ws,
+                              hipStream_t stream) {
+  const int BH = B * Hkv;
+  const int P = (Lc + page_size - 1) / page_size;
+  const int Pcap = (cap + page_size - 1) / page_size;
+  // laid out for the capacity, so a growing cache never moves a head's exchanged words
+  const step::Layout lo = step::layout(B, Hq, Hkv, D, Pcap);
+  const int vmax = dtype == 0 ? vec16<float>::n : vec16<bf16_t>::n;
+  const step::Plan pl = step::plan(BH, P, page_size, n_pages, device_cus(), vmax);
+  if (pl.nb > 1 && (pl.ns > lo.cap_s || pl.na > lo.cap_a))
+    return hipErrorInvalidValue;  // cannot happen: the layout holds the largest plan
+  char* w = static_cast<char*>(ws);
+  step::Args a{};
+  a.q = q;
+  a.kmin_t = kmin_t;
+  a.kmax_t = kmax_t;
+  a.k_c = k_c;
+  a.v_c = v_c;
+  a.BH = BH;
+  a.Hkv = Hkv;
+  a.Lc = Lc;
+  a.ps = page_size;
+  a.n_pages = n_pages;
+  a.P = P;
+  a.r = r;
+  a.ns = pl.ns;
+  a.na = pl.na;
+  a.nb = pl.nb;
+  a.ppb1 = pl.ppb1;
+  a.pps = pl.pps;
+  a.vec = Pcap % vmax == 0;
+  a.cap_s = lo.cap_s;
+  a.cap_a = lo.cap_a;
+  a.kv_pitch = kv_pitch;
+  a.rows = rows;
+  a.s_pitch = Pcap;
+  a.scale2 = scale * kLog2e;
+  a.wait_ticks = wait_ticks();
+  a.chan_idx = chan_idx;
+  a.page_scores = page_scores;
+  a.page_idx = page_idx;
+  a.xscores = reinterpret_cast<uint64_t*>(w + lo.off_xscores);
+  a.xext = reinterpret_cast<uint64_t*>(w + lo.off_xext);
+  a.xpart = reinterpret_cast<uint64_t*>(w + lo.off_xpart);
+  a.sync = reinterpret_cast<unsigned*>(w + lo.off_sync);
+  a.out = out;
+  const int G = Hq / Hkv;
+  return dtype == 0 ? step_launch_f32(D, G, a, stream) : step_launch_bf16(D, G, a, stream);
+}
+
+}  // namespace rkv

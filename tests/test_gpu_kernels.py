@@ -408,6 +408,82 @@ def test_limits_at_their_maximum(rkv):
     _evict_check(rkv, we, gen.prompt_layer(we), needles=False)
 
 
+# Shapes whose plans cover the fused step's role mixes on a 256-CU device: one attender with 32
+# scorers (B*Hkv = 8, top-k 128, the 128K workload's plan), 8 and 16 attenders merged by the last
+# to arrive, one scorer that also attends beside a second attender (B*Hkv = 128, the batch-16
+# workload's plan), ragged page counts, a group of 8 with two merge rounds, fp32, and one block
+# per head (B*Hkv >= 256).
+PLAN_CASES = [
+    # name, dtype, B, Hq, Hkv, D, P, ps, top-k budgets
+    ("bh8-p4096", "bf16", 1, 32, 8, 128, 4096, 4, (128, 512, 1024, 2048)),
+    ("bh128-p1024", "bf16", 16, 32, 8, 128, 1024, 4, (256, 64)),
+    ("bh9-ragged", "bf16", 3, 12, 3, 64, 777, 3, (3, 300, 1500)),
+    ("g8-bh1", "bf16", 1, 8, 1, 128, 2000, 2, (1200, 130)),
+    ("fp32-bh4", "fp32", 2, 4, 2, 64, 500, 2, (200, 998)),
+    ("bh320-solo", "bf16", 40, 32, 8, 64, 300, 4, (512,)),
+]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_fused_decode_step_plans(rkv, case):
+    name, dtype, B, Hq, Hkv, D, P, ps, budgets = case
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Lc = P * ps - (1 if ps > 1 else 0)  # a partial last page
+    w = configs.SMALL[1].replace(name=name, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, L=Lc, keep=Lc,
+                                 page_size=ps, r=D // 4, cfg_id=45)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    k_c = torch.randn((B, Hkv, Lc, D), device="cuda", generator=g).to(dt)
+    v_c = torch.randn((B, Hkv, Lc, D), device="cuda", generator=g).to(dt)
+    q = torch.randn((B, Hq, D), device="cuda", generator=g).to(dt)
+    kmin, kmax = rkv.rkv_build_page_summaries(k_c, ps)
+    G = Hq // Hkv
+    q64 = O.widen(H(q))
+    heads = sorted({(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)})
+    for topk in budgets:
+        out, pages, _ = _fused_vs_calls(rkv, w, q, k_c, v_c, kmin, kmax, topk)
+        got, pg = O.widen(H(out)), pages.cpu().numpy()
+        for (b, h) in heads:
+            toks = O.page_tokens(pg[b, h], ps, Lc)
+            ref = O.sparse_attention(q64[b, h * G:(h + 1) * G], O.widen(H(k_c[b, h])),
+                                     O.widen(H(v_c[b, h])), toks, 1 / math.sqrt(D))
+            assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT[dtype],
+                              f"{name} b{b} h{h} k{topk}")
+
+
+def test_fused_decode_step_beside_a_busy_stream(rkv):
+    # The blocks of a head take their roles from tickets and only wait for blocks that started
+    # before them, so fused steps finish with correct results while another stream's kernels
+    # hold CUs at the same time. The outputs equal those of the same steps run alone.
+    w = configs.SMALL[1].replace(name="busy", B=1, Hq=32, Hkv=8, D=128, L=8192, keep=8192,
+                                 page_size=4, r=32, cfg_id=46)
+    g = torch.Generator(device="cuda").manual_seed(23)
+    k_c = torch.randn((1, 8, w.Lc, 128), device="cuda", generator=g).to(torch.bfloat16)
+    v_c = torch.randn((1, 8, w.Lc, 128), device="cuda", generator=g).to(torch.bfloat16)
+    qs = torch.randn((12, 1, 32, 128), device="cuda", generator=g).to(torch.bfloat16)
+    kmin, kmax = rkv.rkv_build_page_summaries(k_c, 4)
+    n_pages = 256
+    ws = rkv.rkv_hybrid_decode_workspace(qs[0], 8, w.Lc, 4, n_pages)
+    alone = [rkv.rkv_hybrid_decode_step(qs[s], kmin, kmax, k_c, v_c, 4, 32, n_pages, workspace=ws)
+             for s in range(12)]
+    torch.cuda.synchronize()
+    a = torch.randn((4096, 4096), device="cuda", generator=g).to(torch.bfloat16)
+    busy = torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(busy):
+        acc = a
+        for _ in range(6):
+            acc = torch.mm(acc, a) * 1e-3
+    for s in range(12):
+        outs.append(rkv.rkv_hybrid_decode_step(qs[s], kmin, kmax, k_c, v_c, 4, 32, n_pages,
+                                               workspace=ws))
+    torch.cuda.synchronize()
+    assert rkv.decode_workspace_status(ws) == 0
+    for s in range(12):
+        assert torch.equal(outs[s], alone[s]), f"step {s}"
+    del acc
+
+
 def _tied_keys(B, Hkv, P, ps, D, mode, seed):
     """K caches whose pages repeat, so that page scores tie exactly: every page the same, half
     of the pages the same, or pages in groups of three."""

@@ -1,0 +1,196 @@
+"""Host emulation of the address arithmetic of the fused decode step (k_decode_step) and of the
+page-summary kernel (k_page_minmax), at the shapes the benchmark runs: the 128K 8B-shaped layer
+over the compressed cache and over the multi-turn view of the full 131072-token cache (row map,
+cache pitch L), the batch-16 layer (128 heads) and the 80-layer 70B-shaped stack (640 heads).
+
+The plan and workspace layout below restate the library's host plan (rkv_step.hpp: step::plan,
+step::layout); the layout's size is checked against rkv_hybrid_decode_workspace_bytes, which pins
+the restatement to the library. Every global index the kernels form is then evaluated for every
+role and thread, on the extents of the buffers the C ABI documents, for several CU counts.
+CPU only: nothing here launches a kernel.
+"""
+import numpy as np
+import pytest
+
+import sparse_kv_cache_snapkv_amd as rkv
+from workloads import configs
+
+THREADS = 512
+MAX_ATT, MAX_SCORE, TARGET = 16, 64, 256
+SOLO_TOKENS, TOKENS_PER_BLOCK = 128, 64
+SYNC_HEADER, HEAD_WORDS = 16, 4
+MAX_PAGES_PER_WINDOW = 1024
+
+
+def plan(BH, P, ps, n_pages, ncu, vmax):
+    budget = ncu // BH
+    ntok = n_pages * ps
+    na = ns = 1
+    if budget >= 2:
+        na = 1 if ntok <= SOLO_TOKENS else max(min(MAX_ATT, budget, -(-ntok // TOKENS_PER_BLOCK)), 1)
+        ns = min(max(budget - na + 1, 1), MAX_SCORE)
+    pps = -(-n_pages // na)
+    na = -(-n_pages // pps)
+    ppb1 = -(-P // ns)
+    ppb1 = -(-ppb1 // vmax) * vmax
+    ns = -(-P // ppb1)
+    return dict(ns=ns, na=na, nb=ns + na - 1, ppb1=ppb1, pps=pps)
+
+
+def align256(x):
+    return (x + 255) & ~255
+
+
+def layout(B, Hq, Hkv, D, Pcap):
+    BH, G = B * Hkv, Hq // Hkv
+    budget = 0 if BH >= TARGET else TARGET // BH
+    lo = dict(off_sync=0, off_xscores=align256((SYNC_HEADER + HEAD_WORDS * BH) * 4))
+    if budget < 2:
+        lo.update(cap_s=1, cap_a=1, off_xext=lo["off_xscores"], off_xpart=lo["off_xscores"],
+                  total=lo["off_xscores"])
+        return lo
+    lo["cap_s"], lo["cap_a"] = min(budget, MAX_SCORE), min(budget, MAX_ATT)
+    lo["off_xext"] = align256(lo["off_xscores"] + BH * Pcap * 8)
+    lo["off_xpart"] = align256(lo["off_xext"] + BH * lo["cap_s"] * 2 * 8)
+    lo["total"] = align256(lo["off_xpart"] + BH * lo["cap_a"] * (G * D + 2 * G) * 8)
+    return lo
+
+
+SHAPES = [
+    # name, B (layers folded), Hq, Hkv, D, Lc, kv_pitch (L with a row map), ps, r, budgets, dtype
+    ("128K", 1, 32, 8, 128, 16384, 16384, 4, 32, (128, 512, 2048), "bf16"),
+    ("128K-MT", 1, 32, 8, 128, 16384, 131072, 4, 32, (128, 512, 2048), "bf16"),
+    ("32K-b16", 16, 32, 8, 128, 4096, 4096, 4, 32, (256,), "bf16"),
+    ("70B-80L", 80, 64, 8, 128, 32768, 32768, 4, 32, (1024,), "bf16"),
+    ("tiny", 1, 4, 2, 64, 512, 512, 4, 16, (128,), "fp32"),
+    ("grown", 1, 32, 8, 128, 16384 + 100, 16384 + 256, 4, 32, (128, 2048), "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_layout_matches_the_library(shape):
+    name, B, Hq, Hkv, D, Lc, pitch, ps, r, budgets, dtype = shape
+    code = 1 if dtype == "bf16" else 0
+    cap = pitch if name == "grown" else Lc
+    for tk in budgets:
+        n_pages = min(tk // ps, -(-Lc // ps))
+        nbytes = rkv.hybrid_decode_workspace_bytes(B, Hq, Hkv, cap, D, ps, n_pages, code)
+        assert nbytes == layout(B, Hq, Hkv, D, -(-cap // ps))["total"]
+
+
+@pytest.mark.parametrize("ncu", [256, 304, 120, 8])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_fused_step_indices_stay_in_their_buffers(shape, ncu):
+    name, B, Hq, Hkv, D, Lc, pitch, ps, r, budgets, dtype = shape
+    ncu = min(ncu, TARGET)  # the library caps the CU count at 256
+    e = 2 if dtype == "bf16" else 4
+    V = 16 // e  # elements per 16-byte vector
+    BH, G = B * Hkv, Hq // Hkv
+    P = -(-Lc // ps)
+    cap = pitch if name == "grown" else Lc
+    Pcap = -(-cap // ps)
+    s_pitch = Pcap
+    rows_mapped = name.endswith("MT")
+    kv_rows = pitch  # token rows per head of k_c / v_c (the full cache with a row map)
+    lo = layout(B, Hq, Hkv, D, Pcap)
+    tid = np.arange(THREADS)
+    for tk in budgets:
+        n_pages = min(tk // ps, P)
+        pl = plan(BH, P, ps, n_pages, ncu, V)
+        ns, na, nb, ppb1, pps = pl["ns"], pl["na"], pl["nb"], pl["ppb1"], pl["pps"]
+        assert nb * BH <= max(ncu, BH), "a waiting plan fits one block per CU"
+        if nb > 1:
+            assert ns <= lo["cap_s"] and na <= lo["cap_a"]
+        # control words: kSyncHeader + kHeadWords * bh + 2 < words before the score area
+        assert (SYNC_HEADER + HEAD_WORDS * (BH - 1) + 2) * 4 < max(lo["off_xscores"], 4 * (SYNC_HEADER + HEAD_WORDS * BH))
+        E = 8 if P <= 8 * THREADS else 16
+        assert P <= E * THREADS
+        for bh in (0, BH - 1):
+            for rank in range(nb):
+                # scorer: summary rows of the chosen channels (c < D), 16-byte vectors of pages
+                if rank < ns:
+                    pb_lo, pb_hi = rank * ppb1, min(P, rank * ppb1 + ppb1)
+                    assert 0 <= pb_lo < pb_hi <= P
+                    vec = Pcap % V == 0
+                    last = (pb_lo + (-(-(pb_hi - pb_lo) // V) - 1) * V + V - 1) if vec else pb_hi - 1
+                    assert last < s_pitch
+                    top = (bh * D * s_pitch) + (D - 1) * s_pitch + last
+                    assert top < BH * D * s_pitch
+                    if nb > 1:
+                        assert bh * P + pb_hi - 1 < BH * Pcap  # tagged scores
+                        assert ((bh * lo["cap_s"] + rank) * 2 + 1) * 8 + lo["off_xext"] <= lo["off_xpart"]
+                if rank < ns - 1:
+                    continue
+                slice_ = rank - (ns - 1)
+                assert 0 <= slice_ < na
+                # attender: every score word, the extremes of every share
+                j = np.arange(E)[:, None]
+                idx = np.minimum(j * THREADS + tid[None, :], P - 1)
+                assert idx.max() < P and bh * P + idx.max() < BH * Pcap
+                assert (bh * lo["cap_s"] + min(63, ns - 1)) * 2 + 1 < BH * lo["cap_s"] * 2 or nb == 1
+                # its slice of the page list and the token rows of those pages
+                p_lo, p_hi = slice_ * pps, min(slice_ * pps + pps, n_pages)
+                assert 0 <= p_lo and p_hi <= n_pages
+                for w0 in range(p_lo, max(p_hi, p_lo + 1), MAX_PAGES_PER_WINDOW):
+                    nw = min(MAX_PAGES_PER_WINDOW, max(p_hi - w0, 0))
+                    assert nw <= MAX_PAGES_PER_WINDOW  # LDS page slots
+                # a listed page p < P covers slots p*ps + u < Lc; with a row map the slot indexes
+                # rows[bh*Lc + t] (t < Lc), whose value is clamped into [0, kv_pitch)
+                t_max = Lc - 1
+                assert bh * Lc + t_max < BH * Lc
+                row_max = (kv_rows - 1) if rows_mapped else t_max
+                assert (bh * kv_rows + row_max) * D + (D - V) + V - 1 < BH * kv_rows * D
+                # the partial slot and the merger's reads
+                if na > 1:
+                    stride = G * D + 2 * G
+                    top = (bh * lo["cap_a"] + slice_) * stride + stride - 1
+                    assert top * 8 + lo["off_xpart"] < lo["total"]
+                # outputs
+                assert bh * G * D + G * D - 1 < BH * G * D
+                assert bh * n_pages + n_pages - 1 < BH * n_pages
+                assert bh * r + r - 1 < BH * r
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_page_minmax_indices_stay_in_their_buffers(shape):
+    # grid (ceil(P/32), BH) of 256 threads; each thread folds kItems (page, chunk) items over
+    # the page's valid slots, reading row r(t) of the cache, then writes channel rows of s_pitch
+    name, B, Hq, Hkv, D, Lc, pitch, ps, r, budgets, dtype = shape
+    e = 2 if dtype == "bf16" else 4
+    V = 16 // e
+    CH = D // V
+    BH = B * Hkv
+    P = -(-Lc // ps)
+    cap = pitch if name == "grown" else Lc
+    s_pitch = -(-cap // ps)
+    kv_rows = pitch
+    pages_per_block = 32
+    items = pages_per_block * CH // 256
+    tid = np.arange(256)
+    for bx in (0, -(-P // pages_per_block) - 1):
+        p0 = bx * pages_per_block
+        for i in range(items):
+            idx = i * 256 + tid
+            p = p0 + idx // CH
+            t0 = p * ps
+            nt = np.where(p < P, np.minimum(ps, Lc - t0), 0)
+            assert (nt >= 0).all()
+            valid = nt > 0
+            t_last = t0 + nt - 1
+            assert (t_last[valid] < Lc).all()
+            ch = idx % CH
+            row = np.minimum(t_last, kv_rows - 1)
+            assert ((BH - 1) * kv_rows * D + row[valid] * D + ch[valid] * V + V - 1
+                    < BH * kv_rows * D).all()
+        np_ = min(pages_per_block, P - p0)
+        assert (BH - 1) * D * s_pitch + p0 + (D - 1) * s_pitch + np_ - 1 < BH * D * s_pitch
+
+
+def test_library_plans_of_the_benchmarked_workloads():
+    # the plans the benchmark runs on a 256-CU device, written out
+    assert plan(8, 4096, 4, 32, 256, 8) == dict(ns=32, na=1, nb=32, ppb1=128, pps=32)
+    assert plan(8, 4096, 4, 128, 256, 8) == dict(ns=25, na=8, nb=32, ppb1=168, pps=16)
+    assert plan(8, 4096, 4, 512, 256, 8) == dict(ns=17, na=16, nb=32, ppb1=248, pps=32)
+    assert plan(128, 1024, 4, 64, 256, 8) == dict(ns=1, na=2, nb=2, ppb1=1024, pps=32)
+    assert plan(640, 8192, 4, 256, 256, 8) == dict(ns=1, na=1, nb=1, ppb1=8192, pps=256)
+    assert configs.LLAMA8B_128K.P == 4096 and configs.LLAMA70B_256K_80L.P == 8192
