@@ -207,17 +207,18 @@ int rkv_sparse_attend_decode(const void* q, const void* k_c, const void* v_c,
  * ws          rkv_hybrid_decode_workspace_bytes(...) bytes (its size depends on the shape B,
  *             Hq, Hkv, Lc, D, page_size and dtype, not on n_pages), zero-filled ONCE by
  *             rkv_hybrid_decode_workspace_init before its first use, and again before it is used
- *             for a different shape. The workspace holds, per KV head, a call counter and two
- *             ticket counters. The blocks of a head take their roles in the order they start (a
- *             ticket), exchange scores and partial results through the workspace as 64-bit words
- *             tagged with the call counter, and wait only for blocks that started before them; so
- *             a call finishes however its blocks are scheduled, also while other work shares the
- *             GPU, and the block that finishes a head leaves its counters ready for the next call
- *             (no call has to clear anything). Each wait is bounded by about 1 ms of wall-clock
- *             time; a wait that runs out (a block stalled far beyond the step's own duration)
- *             sets a bit of the workspace's status word and the call's output is not valid: read
- *             it with rkv_hybrid_decode_status, and initialise the workspace again before reusing
- *             it. Calls that overlap in time must not share a workspace; calls on different
+ *             for a different shape. The workspace holds, per KV head, a call counter and a
+ *             count of started blocks. The blocks of a head exchange scores and partial results
+ *             through the workspace as 64-bit words tagged with the call counter, and a block
+ *             that still misses another block's result after about 20 us of wall-clock time
+ *             (the environment variable RKV_STEAL_US, read at each call, sets this deadline)
+ *             computes it itself (bit-identical); so a call finishes however its blocks are
+ *             scheduled, also while other work shares the GPU, and leaves the counters ready for
+ *             the next call (no call has to clear anything). Waits for words that must already be
+ *             on their way are bounded by about 1 ms; one that runs out sets a bit of the
+ *             workspace's status word and that call's output is not valid: read it with
+ *             rkv_hybrid_decode_status, and initialise the workspace again before reusing it.
+ *             Calls that overlap in time must not share a workspace; calls on different
  *             workspaces may run concurrently on any streams.
  * ------------------------------------------------------------------------------------------ */
 int rkv_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size,
@@ -231,9 +232,10 @@ int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t
 
 /* The fused step's status word: *status (host memory) receives the bits set by calls on this
  * workspace since it was initialised or last cleared: 1 = a wait for page scores ran out of time,
- * 2 = a wait for attention partials ran out of time, 4 = a block drew a ticket beyond its call's
- * plan (counters left inconsistent by an earlier failed call). 0 means every call's output is
- * valid. clear != 0 zeroes the word after reading it. The read is enqueued on `stream` after the
+ * 2 = a wait for attention partials ran out of time (either makes that call's output invalid);
+ * informational, outputs valid: 16 = a block scored pages whose scoring block had not delivered
+ * within the steal deadline, 32 = the same for an attention slice. (status & 15) == 0 means every
+ * call's output is valid. clear != 0 zeroes the word after reading it. The read is enqueued on `stream` after the
  * work already there, and this call SYNCHRONISES the stream before returning. */
 int rkv_hybrid_decode_status(void* ws, size_t ws_bytes, int clear, uint32_t* status, void* stream);
 

@@ -7,6 +7,7 @@ from .api import (  # noqa: F401
     RkvError,
     hybrid_decode_step,
     hybrid_decode_workspace_bytes,
+    DECODE_STATUS_INVALID,
     decode_workspace_status,
     rkv_hybrid_decode_workspace,
     rkv_hybrid_decode_step,

@@ -228,9 +228,14 @@ def rkv_hybrid_decode_workspace(q: torch.Tensor, Hkv: int, Lc: int, page_size: i
     return ws
 
 
+# Status bits of the fused step that make a call's output invalid (the others are informational:
+# a block computed work whose owner had not delivered in time).
+DECODE_STATUS_INVALID = 0xF
+
+
 def decode_workspace_status(ws: torch.Tensor, clear: bool = False) -> int:
     """The fused step's status word through rkv_hybrid_decode_status (synchronises the current
-    stream): 0 when every call on this workspace was valid, else its failure bits."""
+    stream): every call on this workspace was valid when (status & DECODE_STATUS_INVALID) == 0."""
     val = ctypes.c_uint32(0)
     _check("rkv_hybrid_decode_status", _lib.load().rkv_hybrid_decode_status(
         ws.data_ptr(), ws.numel() * ws.element_size(), int(bool(clear)), ctypes.byref(val),

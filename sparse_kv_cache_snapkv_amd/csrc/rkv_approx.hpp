@@ -55,10 +55,18 @@ __device__ __forceinline__ void select_channels_phase1(const ChannelQ<T, G>& cq,
     sh.key[c] = c < D ? (((uint64_t)__float_as_uint(a) + 1ull) << 7) | (uint64_t)(127 - c) : 0ull;
     sh.qb[c] = sq;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
-__device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShared& sh) {
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// before_last_barrier() runs (in every thread) just before the final barrier, so that what it
+// writes to LDS is visible to the whole block on return.
+template <typename Hook = NoHook>
+__device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShared& sh,
+                                                       Hook&& before_last_barrier = Hook{}) {
   const int tid = threadIdx.x;
   if (tid < 2 * kApproxMaxD) {
     const int c = tid % kApproxMaxD, half = tid / kApproxMaxD;
@@ -71,7 +79,7 @@ __device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShar
     }
     sh.rank[half][c] = above;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < kWave) {
     const int lane = tid;
     const bool t0 = lane < D && sh.rank[0][lane] + sh.rank[1][lane] < (unsigned)r;
@@ -90,7 +98,8 @@ __device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShar
       sh.qc[pos] = sh.qb[lane + kWave];
     }
   }
-  __syncthreads();
+  before_last_barrier();
+  lds_barrier();
 }
 
 template <typename T, int G>

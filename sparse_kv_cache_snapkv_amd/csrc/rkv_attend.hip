@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a) {
   st.init(static_cast<const T*>(a.q) + (size_t)bh * G * D, a.scale2);
   st.run(static_cast<const T*>(a.k_c) + (size_t)bh * a.Lc * D,
          static_cast<const T*>(a.v_c) + (size_t)bh * a.Lc * D, sh.pages, np_blk * a.ps, a.ps, a.P,
-         a.Lc);
+         a.Lc, nullptr, 0, sh);
   st.publish(sh);
   __syncthreads();
   T* out = static_cast<T*>(a.out);

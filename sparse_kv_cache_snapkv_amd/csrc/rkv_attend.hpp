@@ -33,7 +33,30 @@ struct AttendShared {
   int pages[kMaxPagesPerSplit + kWave];  // slots from kMaxPagesPerSplit: discarded writes, per lane
   float m[NW][G], l[NW][G];
   float o[NW][G][D];
+  __align__(16) float px[NW][4][32];  // per wave and row of 16 lanes: a chunk's weights (RS path)
+  __align__(16) float fx[NW][4][8];   // and its per-head rescaling factors
 };
+
+// Reduce-scatter step inside a row of 16 lanes: lanes paired by the DPP pattern CTRL (an
+// involution), the lane with `upper` set keeps the upper half of the N values, its partner the
+// lower half, each adding the partner's copy of the half it keeps.
+// Applies to the first NA values of v.
+template <int CTRL, int NA, int N>
+__device__ __forceinline__ void rs_step(float (&v)[N], bool upper) {
+  static_assert(NA <= N && NA % 2 == 0, "values in the step");
+#pragma unroll
+  for (int i = 0; i < NA / 2; ++i) {
+    const float send = upper ? v[i] : v[i + NA / 2];
+    const float keep = upper ? v[i + NA / 2] : v[i];
+    v[i] = keep + dpp<CTRL>(send);
+  }
+}
+
+// Lanes i <- i + R (mod 16) inside each row.
+template <int R>
+__device__ __forceinline__ float dpp_ror(float v) {
+  return dpp<0x120 + R>(v);
+}
 
 // Per-wave online-softmax state of the G heads of a group; NW waves share a block's page list and
 // each issues SLOTS K and V row loads per chunk. bf16 scores are packed bf16 dot products of the
@@ -46,6 +69,17 @@ struct WaveState {
   uint4 qraw[G];
   float sc2;     // scale * log2(e)
   bool started;  // a chunk has been accumulated (before it, rescaling zeros is skipped)
+
+  // Reduce-scatter path (bf16 rows of 16 lanes, SLOTS*G a multiple of 16): the SLOTS*G partial
+  // dot products of a row are summed by a reduce-scatter, so that lane li finishes NH of them
+  // (slot li / PG, heads (li % PG) * NH + t) and takes one exponential each instead of every
+  // lane taking all of them; the weights reach the row through LDS. m and l below then hold the
+  // running max and sum of the lane's NH heads.
+  static constexpr bool kRS = kBf16 && Geo<T, D, SLOTS>::LPT == 16 && (SLOTS * G) % 16 == 0 &&
+                              16 % SLOTS == 0 && G <= 8;
+  static constexpr int NV = SLOTS * G;      // partial dot products per lane and chunk
+  static constexpr int NH = NV / 16;        // of them finished by each lane
+  static constexpr int PG = 16 / SLOTS;     // lanes of a row between two with the same heads
 
   // The lane's slices of the G queries, as loaded; init(scale2) converts them.
   __device__ __forceinline__ void load_q(const T* __restrict__ q_bh) {
@@ -83,14 +117,24 @@ struct WaveState {
   // into [0, row_hi] (the multi-turn variant keeps the whole cache and indexes its kept rows).
   __device__ __forceinline__ void run(const T* __restrict__ kc_bh, const T* __restrict__ vc_bh,
                                       const int* pages, int ntok, int ps, int P, int Lc,
-                                      const int32_t* __restrict__ rows = nullptr,
-                                      int row_hi = 0) {
+                                      const int32_t* __restrict__ rows, int row_hi,
+                                      AttendShared<D, G, NW>& shared) {
+    run(kc_bh, vc_bh, pages, ntok, ps, P, Lc, rows, row_hi, shared.px, shared.fx);
+  }
+  __device__ __forceinline__ void run(const T* __restrict__ kc_bh, const T* __restrict__ vc_bh,
+                                      const int* pages, int ntok, int ps, int P, int Lc,
+                                      const int32_t* __restrict__ rows, int row_hi,
+                                      float (&px)[NW][4][32], float (&fx)[NW][4][8]) {
     constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT, TPL = Geo<T, D, SLOTS>::TPL;
     constexpr int WTOK = Geo<T, D, SLOTS>::WTOK;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int lg = lane / LPT, li = lane % LPT;
     const T* kb = kc_bh + li * V;
     const T* vb = vc_bh + li * V;
+    if constexpr (kRS) {
+      run_rs(kb, vb, pages, ntok, ps, P, Lc, rows, row_hi, px, fx);
+      return;
+    }
     for (int c0 = wave * WTOK; c0 < ntok; c0 += NW * WTOK) {
       int tok[SLOTS];
       bool ok[SLOTS];
@@ -178,8 +222,125 @@ struct WaveState {
     }
   }
 
+  __device__ __forceinline__ void run_rs(const T* __restrict__ kb, const T* __restrict__ vb,
+                                         const int* pages, int ntok, int ps, int P, int Lc,
+                                         const int32_t* __restrict__ rows, int row_hi,
+                                         float (&px)[NW][4][32], float (&fx)[NW][4][8]) {
+    constexpr int V = Geo<T, D, SLOTS>::V, TPL = Geo<T, D, SLOTS>::TPL;
+    constexpr int WTOK = Geo<T, D, SLOTS>::WTOK;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lg = lane / 16, li = lane % 16;
+    const int slot_l = li / PG;  // the slot whose scores this lane finishes
+    float* prow = px[wave][lg];
+    float* frow = fx[wave][lg];
+    for (int c0 = wave * WTOK; c0 < ntok; c0 += NW * WTOK) {
+      int tok[SLOTS];
+      unsigned okmask = 0u;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const int ti = c0 + s * TPL + lg;
+        bool valid = ti < ntok;
+        const int page = valid ? pages[ti / ps] : 0;
+        const int t = page * ps + ti % ps;
+        valid = valid && page >= 0 && page < P && t < Lc;
+        okmask |= valid ? (1u << s) : 0u;
+        tok[s] = valid ? t : 0;
+      }
+      if (rows != nullptr) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) tok[s] = min(max(rows[tok[s]], 0), row_hi);
+      }
+      uint4 kr[SLOTS], vr[SLOTS];
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        kr[s] = load16_stream(kb + (size_t)tok[s] * D);
+        vr[s] = load16_stream(vb + (size_t)tok[s] * D);
+      }
+      float d[NV];
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s)
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[s * G + g] = dot8_bf16(qraw[g], kr[s]);
+      // reduce-scatter over the row: lane li ends with the sums of d[li*NH .. li*NH + NH)
+      rs_step<kDppRor8, NV>(d, (li & 8) != 0);
+      rs_step<kDppHalfMirror, NV / 2>(d, (li & 4) != 0);
+      rs_step<kDppXor2, NV / 4>(d, (li & 2) != 0);
+      rs_step<kDppXor1, NV / 8>(d, (li & 1) != 0);
+      const bool ok = (okmask >> slot_l) & 1u;
+      float sc[NH], mx[NH];
+#pragma unroll
+      for (int t = 0; t < NH; ++t) {
+        sc[t] = ok ? d[t] * sc2 : -INFINITY;
+        mx[t] = sc[t];
+      }
+      // the chunk's max of each head: over the lanes of the row with the same heads (li mod PG),
+      // then over the wave's four rows
+#pragma unroll
+      for (int t = 0; t < NH; ++t) {
+        if constexpr (PG <= 4) mx[t] = fmaxf(mx[t], dpp_ror<(PG <= 4 ? 4 : 1)>(mx[t]));
+        if constexpr (PG <= 2) mx[t] = fmaxf(mx[t], dpp_ror<(PG <= 2 ? 2 : 1)>(mx[t]));
+        if constexpr (PG <= 1) mx[t] = fmaxf(mx[t], dpp_ror<1>(mx[t]));
+        mx[t] = fmaxf(mx[t], dpp_ror<8>(mx[t]));
+        mx[t] = xor16_step(mx[t], OpMax{});
+        mx[t] = xor32_step(mx[t], OpMax{});
+      }
+      float p[NH], f[NH];
+#pragma unroll
+      for (int t = 0; t < NH; ++t) {
+        const float mn = fmaxf(m[t], mx[t]);
+        f[t] = mn == -INFINITY ? 1.f : exp2_hw(m[t] - mn);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        p[t] = exp2_hw(sc[t] - mu);
+        l[t] = l[t] * f[t] + p[t];
+        m[t] = mn;
+      }
+      // weights (slot, head) and the heads' rescaling factors to every lane of the row (a wave's
+      // LDS accesses complete in order, so no barrier)
+#pragma unroll
+      for (int t = 0; t < NH; ++t) prow[li * NH + t] = p[t];
+      if (li < PG) {
+#pragma unroll
+        for (int t = 0; t < NH; ++t) frow[li * NH + t] = f[t];
+      }
+      float pw[NV], fg[G];
+#pragma unroll
+      for (int v = 0; v < NV; v += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(prow + v);
+        pw[v] = x.x;
+        pw[v + 1] = x.y;
+        pw[v + 2] = x.z;
+        pw[v + 3] = x.w;
+      }
+      // `started` is the same in every lane; until the first chunk, acc is zero
+      if (__builtin_amdgcn_readfirstlane((int)started)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) fg[g] = frow[g];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[g][e] *= fg[g];
+      }
+      started = true;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        float vf[V];
+        unpack16<T>(vr[s], vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float w = pw[s * G + g];
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[g][e] = fmaf(w, vf[e], acc[g][e]);
+        }
+      }
+    }
+  }
+
   // Reduces over the wave's lane groups and stores (m, l, o) of this wave in sh.
   __device__ __forceinline__ void publish(AttendShared<D, G, NW>& sh) {
+    if constexpr (kRS) {
+      publish_rs(sh);
+      return;
+    }
     constexpr int V = Geo<T, D, SLOTS>::V, LPT = Geo<T, D, SLOTS>::LPT;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int lg = lane / LPT, li = lane % LPT;
@@ -199,6 +360,58 @@ struct WaveState {
           sh.l[wave][g] = l[g];
         }
       }
+    }
+  }
+
+  // Reduce-scatter publish: l summed over the lanes holding the same heads and over the rows;
+  // acc summed over the four rows by permlane swaps that leave each lane a quarter of the sums.
+  __device__ __forceinline__ void publish_rs(AttendShared<D, G, NW>& sh) {
+    constexpr int V = Geo<T, D, SLOTS>::V;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int li = lane % 16;
+#pragma unroll
+    for (int t = 0; t < NH; ++t) {
+      float x = l[t];
+      if constexpr (PG <= 4) x += dpp_ror<(PG <= 4 ? 4 : 1)>(x);
+      if constexpr (PG <= 2) x += dpp_ror<(PG <= 2 ? 2 : 1)>(x);
+      if constexpr (PG <= 1) x += dpp_ror<1>(x);
+      x += dpp_ror<8>(x);
+      x = xor16_step(x, OpSum{});
+      x = xor32_step(x, OpSum{});
+      l[t] = x;
+    }
+    if (lane < PG) {  // row 0, lanes holding every head once
+#pragma unroll
+      for (int t = 0; t < NH; ++t) {
+        sh.m[wave][lane * NH + t] = m[t];
+        sh.l[wave][lane * NH + t] = l[t];
+      }
+    }
+    constexpr int NA = G * V;  // accumulators per lane: (head, element) at g*V + e
+    float a[NA];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < V; ++e) a[g * V + e] = acc[g][e];
+    // rows {0,1} against {2,3}: lanes below 32 keep the first half of the values
+#pragma unroll
+    for (int i = 0; i < NA / 2; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]),
+                                                      __float_as_uint(a[i + NA / 2]), false, false);
+      a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // rows 0 against 1 and 2 against 3: lanes with bit 4 clear keep the first half
+#pragma unroll
+    for (int i = 0; i < NA / 4; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]),
+                                                      __float_as_uint(a[i + NA / 4]), false, false);
+      a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const int base = ((lane & 32) ? NA / 2 : 0) + ((lane & 16) ? NA / 4 : 0);
+#pragma unroll
+    for (int i = 0; i < NA / 4; ++i) {
+      const int f = base + i, g = f / V, e = f % V;
+      sh.o[wave][g][li * V + e] = a[i];
     }
   }
 };

@@ -262,6 +262,16 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Block barrier that orders LDS only. __syncthreads() also waits until every global load and store
+// the wave has issued is complete; where a block communicates only through LDS (cross-block data
+// moves through tagged device-coherent words, which need no ordering), that wait would put the
+// acknowledgement of every earlier global store on the critical path.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 2^x by the hardware instruction alone (v_exp_f32): results below the smallest normal float

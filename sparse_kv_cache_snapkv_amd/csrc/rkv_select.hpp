@@ -47,7 +47,7 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t& ea
     sh.wa[slot][wave] = ia;
     sh.wb[slot][wave] = ib;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -89,7 +89,7 @@ __device__ __forceinline__ void rank_bin(const uint32_t (&key)[E], int nvalid, u
     sh.cand[m[e] ? slot : (uint32_t)(kSelectCandidates + lane)] = key[e];
     slot += m[e] ? 1u : 0u;
   }
-  __syncthreads();
+  lds_barrier();
   for (uint32_t t = tid; t < nbin; t += THREADS) {
     const uint32_t kt = sh.cand[t];
     uint32_t gt = 0, ge = 0;
@@ -105,7 +105,7 @@ __device__ __forceinline__ void rank_bin(const uint32_t (&key)[E], int nvalid, u
       sh.need = krem - gt;
     }
   }
-  __syncthreads();
+  lds_barrier();
   T = sh.thr;
   need = sh.need;
 }
@@ -135,7 +135,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
   }
   for (int i = tid; i < kValueBins; i += THREADS) sh.vbins[i] = 0u;
   if (tid == 0) sh.ncand = 0;
-  __syncthreads();
+  lds_barrier();
   lo = sh.wa[0][0];
   hi = sh.wb[0][0];
 #pragma unroll
@@ -161,7 +161,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
       bin[e] = min(max((int)((key_float(key[e]) - flo) * inv), 0), kValueBins - 1);
       if (e < nvalid) atomicAdd(&sh.vbins[bin[e]], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     // thread t owns the kValueBins/THREADS bins just below those of thread t-1 (descending)
     constexpr int BPT = kValueBins / THREADS;
     uint32_t c[BPT], local = 0;
@@ -184,7 +184,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
         run += c[j];
       }
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t nbin = sh.binc;
     if (nbin <= (uint32_t)kSelectCandidates) {
       const int bstar = (int)sh.digit;
@@ -195,7 +195,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
   }
   // radix passes from clean histograms (they share LDS with the value bins)
   for (int i = tid; i < 2 * NW * (256 + kWave); i += THREADS) (&sh.hist[0][0][0])[i] = 0u;
-  __syncthreads();
+  lds_barrier();
   int bits = 32 - __clz((int)(lo ^ hi));  // low bits that still vary
   uint32_t prefix = bits >= 32 ? 0u : (lo >> bits) << bits;
   uint32_t mask = bits >= 32 ? 0u : ~((1u << bits) - 1u);
@@ -212,7 +212,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
     // the other buffer (scanned in the previous pass) is cleared for the next one
     for (int i = tid; i < NW * (256 + kWave); i += THREADS) (&sh.hist[buf ^ 1][0][0])[i] = 0u;
     if (tid == 0) sh.ncand = 0;
-    __syncthreads();
+    lds_barrier();
     if (tid < kWave) {
       // lane l owns digits 255-4l .. 252-4l (descending), summed over the waves' histograms
       uint32_t c[4], c4 = 0;
@@ -239,7 +239,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     prefix |= sh.digit << shift;
     mask |= 255u << shift;
     krem -= sh.above;
@@ -255,7 +255,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[E], int nv
   }
   T = prefix;
   need_eq = krem;
-  __syncthreads();  // the last pass's reads of sh.digit / sh.above precede later writes
+  lds_barrier();  // the last pass's reads of sh.digit / sh.above precede later writes
 }
 
 // Ascending positions of the selected elements. emit(pos, index, selected) is called for every
@@ -392,7 +392,7 @@ __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int 
       sh.wmin[wave] = lo;
       sh.wmax[wave] = hi;
     }
-    __syncthreads();
+    lds_barrier();
     lo = sh.wmin[0];
     hi = sh.wmax[0];
 #pragma unroll
@@ -416,7 +416,7 @@ __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int 
       bin[e] = min(max((int)((key_float(key[e]) - flo) * inv), 0), kValueBins - 1);
       if (e < nvalid) atomicAdd(&sh.vbins[bin[e]], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     // thread t owns bins kValueBins-1-(t*BPT+i), i < BPT (descending from the top)
     auto read_bins = [&](int t, uint32_t (&c)[BPT]) {
 #pragma unroll
@@ -434,7 +434,7 @@ __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int 
     for (int i = 0; i < BPT; ++i) local += c[i];
     const uint32_t incl = wave_inclusive_scan(local);
     if (lane == kWave - 1) sh.wtot[wave] = incl;
-    __syncthreads();
+    lds_barrier();
     // the wave whose bins reach the k-th key, then (in every wave) the bin within it
     uint32_t before = 0, wabove = 0;
     int wstar = 0;
@@ -487,7 +487,7 @@ __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int 
         if (m[e]) sh.cand[slot] = key[e];
         slot += m[e] ? 1u : 0u;
       }
-      __syncthreads();
+      lds_barrier();
       // every wave ranks the bin's keys (lane l: keys l, l+64, ...) against each other
       const uint32_t krem = k - above;
       uint32_t tsel = 0, nsel = 0, esel = 0;
@@ -566,7 +566,7 @@ __device__ __forceinline__ void strided_positions(const uint32_t (&key)[E], int 
 #pragma unroll
       for (int e = 0; e < E; ++e) sh.gtc[e * NW + wave] = (uint32_t)__popcll(bt[e]);
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t tk[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -594,7 +594,7 @@ __device__ __forceinline__ void strided_positions(const uint32_t (&key)[E], int 
       sh.eqc[e * NW + wave] = (uint32_t)__popcll(be[e]);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // every wave scans the table: lane l holds entries l*R .. l*R+R-1
   uint32_t tg[R], te[R], le = 0;
 #pragma unroll

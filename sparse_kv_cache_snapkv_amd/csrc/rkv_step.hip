@@ -1,5 +1,7 @@
 // Host side of the fused decode step (rkv_step.hpp): plan, workspace layout, launch, and the
 // workspace's initialisation and status word.
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "rkv_launch.hpp"
@@ -9,7 +11,11 @@ namespace rkv {
 
 namespace {
 
-constexpr int kWaitMicroseconds = 1000;  // bound of one cross-block wait
+// A waiting block does the missing work itself after this many microseconds; the environment
+// variable RKV_STEAL_US overrides it (0 makes every wait steal at once, which tests use to run
+// the stealing paths).
+constexpr int kStealMicroseconds = 20;
+constexpr int kWaitMicroseconds = 1000;  // bound of a wait for words already on their way
 
 __global__ void k_zero_u32(unsigned* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
@@ -17,9 +23,9 @@ __global__ void k_zero_u32(unsigned* p, size_t n) {
     p[i] = 0u;
 }
 
-// Steady-counter ticks per wait bound on the current device (the counter's rate is a device
+// Steady-counter ticks per microsecond on the current device (the counter's rate is a device
 // attribute, in kHz).
-long long wait_ticks() {
+long long ticks_per_us() {
   static long long cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -27,7 +33,7 @@ long long wait_ticks() {
     int khz = 0;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz < 1)
       khz = 100000;  // 100 MHz
-    cache[dev] = (long long)khz * kWaitMicroseconds / 1000;
+    cache[dev] = std::max<long long>(1, khz / 1000);
   }
   return cache[dev];
 }
@@ -72,7 +78,7 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   const step::Layout lo = step::layout(B, Hq, Hkv, D, Pcap);
   const int vmax = dtype == 0 ? vec16<float>::n : vec16<bf16_t>::n;
   const step::Plan pl = step::plan(BH, P, page_size, n_pages, device_cus(), vmax);
-  if (pl.nb > 1 && (pl.ns > lo.cap_s || pl.na > lo.cap_a))
+  if (pl.nb > 1 && (pl.ns > step::kMaxScorers || pl.na > lo.cap_a))
     return hipErrorInvalidValue;  // cannot happen: the layout holds the largest plan
   char* w = static_cast<char*>(ws);
   step::Args a{};
@@ -94,18 +100,19 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   a.ppb1 = pl.ppb1;
   a.pps = pl.pps;
   a.vec = Pcap % vmax == 0;
-  a.cap_s = lo.cap_s;
   a.cap_a = lo.cap_a;
   a.kv_pitch = kv_pitch;
   a.rows = rows;
   a.s_pitch = Pcap;
   a.scale2 = scale * kLog2e;
-  a.wait_ticks = wait_ticks();
+  const char* steal_env = getenv("RKV_STEAL_US");
+  const long long steal_us = steal_env != nullptr ? std::max(0L, atol(steal_env)) : kStealMicroseconds;
+  a.steal_ticks = ticks_per_us() * steal_us;
+  a.wait_ticks = ticks_per_us() * kWaitMicroseconds;
   a.chan_idx = chan_idx;
   a.page_scores = page_scores;
   a.page_idx = page_idx;
   a.xscores = reinterpret_cast<uint64_t*>(w + lo.off_xscores);
-  a.xext = reinterpret_cast<uint64_t*>(w + lo.off_xext);
   a.xpart = reinterpret_cast<uint64_t*>(w + lo.off_xpart);
   a.sync = reinterpret_cast<unsigned*>(w + lo.off_sync);
   a.out = out;

@@ -44,7 +44,7 @@ def _decode_gpu(rkv, w, q, k_c, v_c, kmin, kmax, topk, fused=False):
         ws = rkv.rkv_hybrid_decode_workspace(q, Hkv, k_c.shape[2], w.page_size, n_pages)
         fo = rkv.rkv_hybrid_decode_step(q, kmin, kmax, k_c, v_c, w.page_size, w.r, n_pages,
                                         chan_idx=fc, page_scores=fs, page_idx=fp, workspace=ws)
-        assert rkv.decode_workspace_status(ws) == 0
+        assert rkv.decode_workspace_status(ws) & rkv.DECODE_STATUS_INVALID == 0
         assert torch.equal(fc, chans), "fused step channels"
         assert torch.equal(fs.view(torch.int32), scores.view(torch.int32)), "fused step scores"
         assert torch.equal(fp, pages), "fused step pages"

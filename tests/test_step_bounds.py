@@ -23,18 +23,15 @@ MAX_PAGES_PER_WINDOW = 1024
 
 
 def plan(BH, P, ps, n_pages, ncu, vmax):
-    budget = ncu // BH
+    nb0 = max(min(ncu // BH, MAX_SCORE), 1)
     ntok = n_pages * ps
-    na = ns = 1
-    if budget >= 2:
-        na = 1 if ntok <= SOLO_TOKENS else max(min(MAX_ATT, budget, -(-ntok // TOKENS_PER_BLOCK)), 1)
-        ns = min(max(budget - na + 1, 1), MAX_SCORE)
+    na = 1 if ntok <= SOLO_TOKENS else max(min(MAX_ATT, nb0, -(-ntok // TOKENS_PER_BLOCK)), 1)
     pps = -(-n_pages // na)
     na = -(-n_pages // pps)
-    ppb1 = -(-P // ns)
+    ppb1 = -(-P // nb0)
     ppb1 = -(-ppb1 // vmax) * vmax
     ns = -(-P // ppb1)
-    return dict(ns=ns, na=na, nb=ns + na - 1, ppb1=ppb1, pps=pps)
+    return dict(ns=ns, na=na, nb=max(ns, na), ppb1=ppb1, pps=pps)
 
 
 def align256(x):
@@ -46,12 +43,10 @@ def layout(B, Hq, Hkv, D, Pcap):
     budget = 0 if BH >= TARGET else TARGET // BH
     lo = dict(off_sync=0, off_xscores=align256((SYNC_HEADER + HEAD_WORDS * BH) * 4))
     if budget < 2:
-        lo.update(cap_s=1, cap_a=1, off_xext=lo["off_xscores"], off_xpart=lo["off_xscores"],
-                  total=lo["off_xscores"])
+        lo.update(cap_a=1, off_xpart=lo["off_xscores"], total=lo["off_xscores"])
         return lo
-    lo["cap_s"], lo["cap_a"] = min(budget, MAX_SCORE), min(budget, MAX_ATT)
-    lo["off_xext"] = align256(lo["off_xscores"] + BH * Pcap * 8)
-    lo["off_xpart"] = align256(lo["off_xext"] + BH * lo["cap_s"] * 2 * 8)
+    lo["cap_a"] = min(budget, MAX_ATT)
+    lo["off_xpart"] = align256(lo["off_xscores"] + BH * Pcap * 8)
     lo["total"] = align256(lo["off_xpart"] + BH * lo["cap_a"] * (G * D + 2 * G) * 8)
     return lo
 
@@ -99,17 +94,18 @@ def test_fused_step_indices_stay_in_their_buffers(shape, ncu):
         pl = plan(BH, P, ps, n_pages, ncu, V)
         ns, na, nb, ppb1, pps = pl["ns"], pl["na"], pl["nb"], pl["ppb1"], pl["pps"]
         assert nb * BH <= max(ncu, BH), "a waiting plan fits one block per CU"
+        assert ns <= nb and na <= nb
         if nb > 1:
-            assert ns <= lo["cap_s"] and na <= lo["cap_a"]
+            assert ns <= MAX_SCORE and na <= lo["cap_a"]
         # control words: kSyncHeader + kHeadWords * bh + 2 < words before the score area
         assert (SYNC_HEADER + HEAD_WORDS * (BH - 1) + 2) * 4 < max(lo["off_xscores"], 4 * (SYNC_HEADER + HEAD_WORDS * BH))
         E = 8 if P <= 8 * THREADS else 16
         assert P <= E * THREADS
         for bh in (0, BH - 1):
-            for rank in range(nb):
+            for y in range(nb):
                 # scorer: summary rows of the chosen channels (c < D), 16-byte vectors of pages
-                if rank < ns:
-                    pb_lo, pb_hi = rank * ppb1, min(P, rank * ppb1 + ppb1)
+                if y < ns:
+                    pb_lo, pb_hi = y * ppb1, min(P, y * ppb1 + ppb1)
                     assert 0 <= pb_lo < pb_hi <= P
                     vec = Pcap % V == 0
                     last = (pb_lo + (-(-(pb_hi - pb_lo) // V) - 1) * V + V - 1) if vec else pb_hi - 1
@@ -118,33 +114,43 @@ def test_fused_step_indices_stay_in_their_buffers(shape, ncu):
                     assert top < BH * D * s_pitch
                     if nb > 1:
                         assert bh * P + pb_hi - 1 < BH * Pcap  # tagged scores
-                        assert ((bh * lo["cap_s"] + rank) * 2 + 1) * 8 + lo["off_xext"] <= lo["off_xpart"]
-                if rank < ns - 1:
+                        assert (bh * P + pb_hi - 1) * 8 + lo["off_xscores"] < lo["off_xpart"]
+                if y >= na:
                     continue
-                slice_ = rank - (ns - 1)
-                assert 0 <= slice_ < na
-                # attender: every score word, the extremes of every share
+                # attender: every score word; a stale one marks share (page / ppb1) < ns
                 j = np.arange(E)[:, None]
                 idx = np.minimum(j * THREADS + tid[None, :], P - 1)
                 assert idx.max() < P and bh * P + idx.max() < BH * Pcap
-                assert (bh * lo["cap_s"] + min(63, ns - 1)) * 2 + 1 < BH * lo["cap_s"] * 2 or nb == 1
+                assert (idx // ppb1).max() < ns <= 64
                 # its slice of the page list and the token rows of those pages
-                p_lo, p_hi = slice_ * pps, min(slice_ * pps + pps, n_pages)
+                p_lo, p_hi = y * pps, min(y * pps + pps, n_pages)
                 assert 0 <= p_lo and p_hi <= n_pages
-                for w0 in range(p_lo, max(p_hi, p_lo + 1), MAX_PAGES_PER_WINDOW):
-                    nw = min(MAX_PAGES_PER_WINDOW, max(p_hi - w0, 0))
-                    assert nw <= MAX_PAGES_PER_WINDOW  # LDS page slots
                 # a listed page p < P covers slots p*ps + u < Lc; with a row map the slot indexes
                 # rows[bh*Lc + t] (t < Lc), whose value is clamped into [0, kv_pitch)
                 t_max = Lc - 1
                 assert bh * Lc + t_max < BH * Lc
                 row_max = (kv_rows - 1) if rows_mapped else t_max
                 assert (bh * kv_rows + row_max) * D + (D - V) + V - 1 < BH * kv_rows * D
-                # the partial slot and the merger's reads
                 if na > 1:
+                    # its partial, and the words of its merge range: o of (slice, element) at
+                    # i < na*ne (three per thread), (max, sum) of (slice, head) at t < 2*na*G
                     stride = G * D + 2 * G
-                    top = (bh * lo["cap_a"] + slice_) * stride + stride - 1
-                    assert top * 8 + lo["off_xpart"] < lo["total"]
+                    assert ((bh * lo["cap_a"] + y) * stride + stride - 1) * 8 + lo["off_xpart"] < lo["total"]
+                    cpb = -(-(G * D) // na)
+                    e0, ne = y * cpb, min(cpb, G * D - y * cpb)
+                    no = na * ne if ne > 0 else 0
+                    NO = -(-(G * D + MAX_ATT) // THREADS)
+                    assert no <= NO * THREADS and no <= G * D + MAX_ATT
+                    for k in range(NO):
+                        i = np.minimum(tid + k * THREADS, max(no - 1, 0))
+                        sl = i // ne if ne > 0 else 0 * i
+                        e = i - sl * ne if ne > 0 else 0 * i
+                        word = (bh * lo["cap_a"] + sl) * stride + np.minimum(e0 + e, G * D - 1)
+                        assert (sl < na).all() and word.max() * 8 + lo["off_xpart"] < lo["total"]
+                    t = np.minimum(tid, 2 * na * G - 1)
+                    which, rem = t // (na * G), t % (na * G)
+                    word = (bh * lo["cap_a"] + rem // G) * stride + G * D + which * G + rem % G
+                    assert word.max() * 8 + lo["off_xpart"] < lo["total"]
                 # outputs
                 assert bh * G * D + G * D - 1 < BH * G * D
                 assert bh * n_pages + n_pages - 1 < BH * n_pages
@@ -189,8 +195,8 @@ def test_page_minmax_indices_stay_in_their_buffers(shape):
 def test_library_plans_of_the_benchmarked_workloads():
     # the plans the benchmark runs on a 256-CU device, written out
     assert plan(8, 4096, 4, 32, 256, 8) == dict(ns=32, na=1, nb=32, ppb1=128, pps=32)
-    assert plan(8, 4096, 4, 128, 256, 8) == dict(ns=25, na=8, nb=32, ppb1=168, pps=16)
-    assert plan(8, 4096, 4, 512, 256, 8) == dict(ns=17, na=16, nb=32, ppb1=248, pps=32)
-    assert plan(128, 1024, 4, 64, 256, 8) == dict(ns=1, na=2, nb=2, ppb1=1024, pps=32)
+    assert plan(8, 4096, 4, 128, 256, 8) == dict(ns=32, na=8, nb=32, ppb1=128, pps=16)
+    assert plan(8, 4096, 4, 512, 256, 8) == dict(ns=32, na=16, nb=32, ppb1=128, pps=32)
+    assert plan(128, 1024, 4, 64, 256, 8) == dict(ns=2, na=2, nb=2, ppb1=512, pps=32)
     assert plan(640, 8192, 4, 256, 256, 8) == dict(ns=1, na=1, nb=1, ppb1=8192, pps=256)
     assert configs.LLAMA8B_128K.P == 4096 and configs.LLAMA70B_256K_80L.P == 8192
