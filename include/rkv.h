@@ -211,7 +211,8 @@ int rkv_sparse_attend_decode(const void* q, const void* k_c, const void* v_c,
  *             count of started blocks. The blocks of a head exchange scores and partial results
  *             through the workspace as 64-bit words tagged with the call counter, and a block
  *             that still misses another block's result after about 20 us of wall-clock time
- *             (the environment variable RKV_STEAL_US, read at each call, sets this deadline)
+ *             (the environment variable RKV_STEAL_US, read at each call, sets this deadline;
+ *             a negative value makes waiting blocks redo all such work, for testing)
  *             computes it itself (bit-identical); so a call finishes however its blocks are
  *             scheduled, also while other work shares the GPU, and leaves the counters ready for
  *             the next call (no call has to clear anything). Waits for words that must already be

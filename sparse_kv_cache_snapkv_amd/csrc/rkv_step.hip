@@ -12,8 +12,8 @@ namespace rkv {
 namespace {
 
 // A waiting block does the missing work itself after this many microseconds; the environment
-// variable RKV_STEAL_US overrides it (0 makes every wait steal at once, which tests use to run
-// the stealing paths).
+// variable RKV_STEAL_US overrides it (0: after one look; negative: every waiting block redoes all
+// the work it waits for, which tests use to run the stealing paths on every call).
 constexpr int kStealMicroseconds = 20;
 constexpr int kWaitMicroseconds = 1000;  // bound of a wait for words already on their way
 
@@ -106,8 +106,8 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   a.s_pitch = Pcap;
   a.scale2 = scale * kLog2e;
   const char* steal_env = getenv("RKV_STEAL_US");
-  const long long steal_us = steal_env != nullptr ? std::max(0L, atol(steal_env)) : kStealMicroseconds;
-  a.steal_ticks = ticks_per_us() * steal_us;
+  const long long steal_us = steal_env != nullptr ? atol(steal_env) : kStealMicroseconds;
+  a.steal_ticks = steal_us < 0 ? -1 : ticks_per_us() * steal_us;
   a.wait_ticks = ticks_per_us() * kWaitMicroseconds;
   a.chan_idx = chan_idx;
   a.page_scores = page_scores;

@@ -68,7 +68,8 @@ struct Args {
   const int32_t* rows;   // optional [BH, Lc]: slot t of head bh is row rows[bh*Lc + t] of k_c, v_c
   int s_pitch;           // pages per channel row of the summaries (>= P)
   float scale2;          // softmax scale * log2(e)
-  long long steal_ticks; // wait before a block does missing work itself (steady-counter ticks)
+  long long steal_ticks; // wait before a block does missing work itself (steady-counter
+                         // ticks); negative: it does all of it itself (a test mode)
   long long wait_ticks;  // bound of a wait for words that must already be on their way
   int32_t* chan_idx;     // optional [BH, r]
   float* page_scores;    // optional [BH, P]
@@ -241,6 +242,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
       }
       lds_barrier();
       uint64_t missing = ((uint64_t)s_miss_hi << 32) | s_miss_lo;
+      if (a.steal_ticks < 0) missing = a.ns >= 64 ? ~0ull : (1ull << a.ns) - 1ull;  // test mode
       if (missing != 0ull) {
         if (tid == 0) set_status(a.sync, kStatusStoleShare);
         while (missing != 0ull) {  // block-uniform
@@ -376,6 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
       }
       lds_barrier();
       unsigned miss = mg.missing;
+      if (a.steal_ticks < 0) miss = (1u << a.na) - 1u;  // test mode: every slice redone here
       if (miss != 0u) {
         if (tid == 0) set_status(a.sync, kStatusStoleSlice);
         while (miss != 0u) {  // block-uniform

@@ -488,10 +488,10 @@ def test_fused_decode_step_beside_a_busy_stream(rkv):
 @pytest.mark.parametrize("case", [PLAN_CASES[0], PLAN_CASES[1], PLAN_CASES[3]],
                          ids=[PLAN_CASES[i][0] for i in (0, 1, 3)])
 def test_fused_decode_step_stealing(rkv, case, monkeypatch):
-    # With the steal deadline at zero, attenders score the shares and attend the slices whose
-    # owners have not delivered at their first look: the work is done twice, and the results
-    # must still equal the three calls' bit for bit (scores, pages) and the oracle.
-    monkeypatch.setenv("RKV_STEAL_US", "0")
+    # With a negative steal deadline (a test mode), every attender scores every share and
+    # attends every slice itself: the work is done several times over, and the results must
+    # still equal the three calls' bit for bit (scores, pages) and the oracle.
+    monkeypatch.setenv("RKV_STEAL_US", "-1")
     name, dtype, B, Hq, Hkv, D, P, ps, budgets = case
     Lc = P * ps
     w = configs.SMALL[1].replace(name=name, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, L=Lc, keep=Lc,
@@ -517,8 +517,8 @@ def test_fused_decode_step_stealing(rkv, case, monkeypatch):
                                      O.widen(H(v_c[b, h])), toks, 1 / math.sqrt(D))
             assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT[dtype], f"{name} k{topk}")
     # informational bits: 16 = an attender scored a share, 32 = an attender attended a slice
-    # (which of them happens depends on the blocks' timing; some must have)
-    assert stole & (16 | 32), "no work was done by a block other than its owner"
+    assert stole & 16, "no share was scored by an attender"
+    assert stole & 32 or all(min(tk // ps, P) * ps <= 128 for tk in budgets), "no slice redone"
 
 
 def _tied_keys(B, Hkv, P, ps, D, mode, seed):
