@@ -12,8 +12,9 @@
  *   - Pointers are DEVICE pointers to dense row-major arrays unless stated otherwise. The caller
  *     owns every buffer, workspaces included; the library never allocates or frees, and it
  *     synchronises only in rkv_hybrid_decode_status. It keeps no state between calls apart from
- *     what a workspace holds, so concurrent calls on different streams are safe as long as their
- *     output and workspace buffers do not overlap.
+ *     what a workspace holds (and the fixed scratch of rkv_hybrid_decode_step_noalloc), so
+ *     concurrent calls on different streams are safe as long as their output and workspace
+ *     buffers do not overlap (and they are not both rkv_hybrid_decode_step_noalloc on one GPU).
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously.
  *   - dtype: RKV_F32 (float) or RKV_BF16 (bfloat16 stored as uint16 bit patterns). q, K, V,
  *     summaries and attention outputs share the call's dtype; scores, pooled scores and all
@@ -45,7 +46,8 @@ enum rkv_status {
   RKV_ERR_DTYPE = -3,       /* unknown dtype */
   RKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the matching *_workspace_bytes */
   RKV_ERR_UNSUPPORTED = -5, /* valid but not implemented here (e.g. head dim not 64 or 128) */
-  RKV_ERR_LAUNCH = -6       /* the HIP runtime refused to enqueue a kernel */
+  RKV_ERR_LAUNCH = -6,      /* the HIP runtime refused to enqueue a kernel */
+  RKV_ERR_SCRATCH = -7      /* the shape needs more than RKV_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 enum rkv_dtype { RKV_F32 = 0, RKV_BF16 = 1 };
@@ -239,6 +241,33 @@ int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t
  * call's output is valid. clear != 0 zeroes the word after reading it. The read is enqueued on `stream` after the
  * work already there, and this call SYNCHRONISES the stream before returning. */
 int rkv_hybrid_decode_status(void* ws, size_t ws_bytes, int clear, uint32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * rkv_hybrid_decode_step without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, limits, results and errors are those of rkv_hybrid_decode_step, except:
+ *   - The workspace is the library's own scratch: a fixed RKV_NOALLOC_SCRATCH_BYTES (8 MiB) of
+ *     device memory per GPU, part of the loaded library and held until the process ends. A shape
+ *     whose rkv_hybrid_decode_workspace_bytes exceeds it is refused with RKV_ERR_SCRATCH before
+ *     anything is enqueued (every shape with 128 < B*Hkv <= 524000 fits, and so does any with
+ *     B*Hkv*ceil(Lc/page_size) <= 2^19 pages, e.g. 8 heads of 16384-token caches at page 4).
+ *   - The call allocates and frees nothing. On its first call on a device it looks up that
+ *     device's scratch address; whenever B*Hkv, Hq/Hkv, D, ceil(Lc/page_size) or dtype differ
+ *     from the previous call's on the same device (and on the first call), it first enqueues a
+ *     fill kernel that zeroes the part of the scratch the shape uses.
+ *   - Every call on a GPU shares that GPU's scratch and leaves its counters there for the next
+ *     call: calls that overlap in time on one GPU (other streams, other host threads) race and
+ *     their results are undefined. Issue them in order on one stream, or synchronise between.
+ *   - status: NULL, or DEVICE memory for one uint32: after the step the scratch's status word
+ *     (bits as in rkv_hybrid_decode_status) is moved there and cleared. Bits 1 and 2 mark that
+ *     call's output invalid; the counters stay consistent, so later calls are unaffected.
+ * ------------------------------------------------------------------------------------------ */
+#define RKV_NOALLOC_SCRATCH_BYTES (8u << 20)
+int rkv_hybrid_decode_step_noalloc(const void* q, const void* kmin_t, const void* kmax_t,
+                                   const void* k_c, const void* v_c, int B, int Hq, int Hkv,
+                                   int Lc, int D, int page_size, int r, int n_pages, float scale,
+                                   int dtype, int32_t* chan_idx, float* page_scores,
+                                   int32_t* page_idx, void* out, uint32_t* status, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Decode-time append into a compressed cache that grows ([rebuttal] "SCBench Results": plain

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     decode_workspace_status,
     rkv_hybrid_decode_workspace,
     rkv_hybrid_decode_step,
+    rkv_hybrid_decode_step_noalloc,
     rkv_build_page_summaries,
     rkv_build_page_summaries_cap,
     rkv_kv_append,

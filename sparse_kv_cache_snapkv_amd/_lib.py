@@ -31,6 +31,8 @@ SIGNATURES = {
                                           _vp]),
     "rkv_hybrid_decode_step": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int]
                                + [_vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "rkv_hybrid_decode_step_noalloc": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int]
+                                       + [_vp, _vp, _vp, _vp, _vp, _vp]),
     "rkv_build_page_summaries_cap": (_c_int, [_vp] + [_c_int] * 7 + [_vp, _vp, _vp]),
     "rkv_kv_append": (_c_int, [_vp, _vp] + [_c_int] * 7 + [_vp, _vp, _vp, _vp, _vp]),
     "rkv_hybrid_decode_step_cap": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int]

@@ -288,6 +288,39 @@ def rkv_hybrid_decode_step(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.
     return out
 
 
+def rkv_hybrid_decode_step_noalloc(q: torch.Tensor, kmin_t: torch.Tensor, kmax_t: torch.Tensor,
+                                   k_c: torch.Tensor, v_c: torch.Tensor, page_size: int, r: int,
+                                   n_pages: int, scale: Optional[float] = None, *,
+                                   chan_idx: Optional[torch.Tensor] = None,
+                                   page_scores: Optional[torch.Tensor] = None,
+                                   page_idx: Optional[torch.Tensor] = None,
+                                   out: Optional[torch.Tensor] = None,
+                                   status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """rkv_hybrid_decode_step on the library's own per-GPU scratch (no workspace; the C call
+    allocates nothing). status: optional int32 GPU tensor of one element that receives the
+    scratch's status word after the step. Calls that overlap in time on one GPU race."""
+    B, Hq, D = q.shape
+    Hkv, Lc = k_c.shape[1], k_c.shape[2]
+    P = -(-Lc // page_size)
+    _shape(k_c, "k_c", (B, Hkv, Lc, D))
+    _shape(v_c, "v_c", (B, Hkv, Lc, D))
+    _step_shapes(q, kmin_t, kmax_t, Hkv, P, P, r, n_pages, chan_idx, page_scores, page_idx, out)
+    if status is not None and status.numel() != 1:
+        raise ValueError("status must hold one element")
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    opt = lambda t, n, d: _dev(t, n, d) if t is not None else None  # noqa: E731
+    _check("rkv_hybrid_decode_step_noalloc", _lib.load().rkv_hybrid_decode_step_noalloc(
+        _dev(q, "q"), _dev(kmin_t, "kmin_t", q.dtype), _dev(kmax_t, "kmax_t", q.dtype),
+        _dev(k_c, "k_c", q.dtype), _dev(v_c, "v_c", q.dtype), B, Hq, Hkv, Lc, D, page_size, r,
+        n_pages, scale, dt, opt(chan_idx, "chan_idx", torch.int32),
+        opt(page_scores, "page_scores", torch.float32), opt(page_idx, "page_idx", torch.int32),
+        _dev(out, "out", q.dtype), opt(status, "status", torch.int32), _stream(q)))
+    return out
+
+
 # ----------------------------------------------------------------------------- growing caches
 def _cap_shapes(k_c: torch.Tensor, kmin_t: torch.Tensor, page_size: int) -> Tuple[int, int]:
     cap = k_c.shape[2]

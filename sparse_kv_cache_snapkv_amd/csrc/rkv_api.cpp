@@ -104,6 +104,8 @@ const char* rkv_status_string(int status) {
       return "unsupported configuration (head dim must be 64 or 128; see header limits)";
     case RKV_ERR_LAUNCH:
       return "the HIP runtime failed to enqueue a kernel";
+    case RKV_ERR_SCRATCH:
+      return "the shape needs more than the library's fixed scratch (RKV_NOALLOC_SCRATCH_BYTES)";
     default:
       return "unknown status";
   }
@@ -302,6 +304,31 @@ int rkv_hybrid_decode_step(const void* q, const void* kmin_t, const void* kmax_t
                                                Lc, Lc, Lc, D, page_size, r, n_pages, scale, dtype,
                                                chan_idx, page_scores, page_idx, out, ws,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int rkv_hybrid_decode_step_noalloc(const void* q, const void* kmin_t, const void* kmax_t,
+                                   const void* k_c, const void* v_c, int B, int Hq, int Hkv,
+                                   int Lc, int D, int page_size, int r, int n_pages, float scale,
+                                   int dtype, int32_t* chan_idx, float* page_scores,
+                                   int32_t* page_idx, void* out, uint32_t* status, void* stream) {
+  static_assert(rkv::kNoAllocScratchBytes == RKV_NOALLOC_SCRATCH_BYTES, "scratch size");
+  if (!q || !kmin_t || !kmax_t || !k_c || !v_c || !out) return RKV_ERR_NULL;
+  if (!dtype_ok(dtype)) return RKV_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lc < 1 || page_size < 1 || n_pages < 1 || Hq % Hkv)
+    return RKV_ERR_SHAPE;
+  const int P = ceil_div(Lc, page_size);
+  if (n_pages > P || r < 1 || r > D || !isfinite(scale)) return RKV_ERR_SHAPE;
+  if (!dims_ok((long)B * Hkv, Lc, Lc, D)) return RKV_ERR_SHAPE;
+  if (!head_dim_ok(D) || Hq / Hkv > 8 || P > kFusedMaxPages) return RKV_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(kmin_t) ||
+      !aligned16(kmax_t) || (status != nullptr && !aligned16(status)))
+    return RKV_ERR_SHAPE;
+  if (rkv::decode_ws_bytes(B, Hq, Hkv, Lc, D, page_size, n_pages, dtype) >
+      rkv::kNoAllocScratchBytes)
+    return RKV_ERR_SCRATCH;
+  return launch_status(rkv::launch_decode_step_noalloc(
+      q, kmin_t, kmax_t, k_c, v_c, B, Hq, Hkv, Lc, D, page_size, r, n_pages, scale, dtype,
+      chan_idx, page_scores, page_idx, out, status, static_cast<hipStream_t>(stream)));
 }
 
 int rkv_hybrid_decode_step_indexed(const void* q, const void* kmin_t, const void* kmax_t,

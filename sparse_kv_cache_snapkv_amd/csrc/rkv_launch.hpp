@@ -48,8 +48,8 @@ hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
                                 void* ws, hipStream_t stream);
 
 // One fused decode step in a single kernel: approximate page scores, page top-k, attention and
-// split merge; the blocks of a head draw their roles from ticket counters in the workspace and
-// exchange tagged words through it.
+// split merge; the blocks of a head take their roles from their block index and exchange
+// call-tagged words through the workspace.
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int Lc, int D, int page_size, int n_pages,
                        int dtype);
 hipError_t launch_decode_ws_init(void* ws, size_t bytes, hipStream_t stream);
@@ -65,6 +65,19 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
                               int n_pages, float scale, int dtype, int32_t* chan_idx,
                               float* page_scores, int32_t* page_idx, void* out, void* ws,
                               hipStream_t stream);
+
+// The same step with the library's own per-device scratch in place of a workspace, for callers
+// that cannot allocate: a layout of more than kNoAllocScratchBytes is refused (by the caller of
+// launch_decode_step_noalloc), the scratch is cleared whenever the layout differs from the
+// previous call's on the device, and when status is not NULL the status word is moved there
+// (device memory) after the step.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+hipError_t launch_decode_step_noalloc(const void* q, const void* kmin_t, const void* kmax_t,
+                                      const void* k_c, const void* v_c, int B, int Hq, int Hkv,
+                                      int Lc, int D, int page_size, int r, int n_pages,
+                                      float scale, int dtype, int32_t* chan_idx,
+                                      float* page_scores, int32_t* page_idx, void* out,
+                                      uint32_t* status, hipStream_t stream);
 
 // SnapKV++ eviction.
 size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype);

@@ -3,6 +3,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "rkv_launch.hpp"
 #include "rkv_step.hpp"
@@ -118,6 +119,85 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   a.out = out;
   const int G = Hq / Hkv;
   return dtype == 0 ? step_launch_f32(D, G, a, stream) : step_launch_bf16(D, G, a, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Allocation-free variant. The scratch below stands in for the workspace; each device holds its
+// own copy from the library's load until the process ends. Host code never uses the array's name
+// as an address: the device address comes from hipGetSymbolAddress, once per device.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// What fixes the workspace layout and the heads whose call counters advance together; a call
+// whose key differs from the previous call's on the device starts from a cleared scratch.
+struct ScratchKey {
+  int BH = 0, G = 0, D = 0, Pcap = 0, dtype = -1;
+  bool operator==(const ScratchKey& o) const {
+    return BH == o.BH && G == o.G && D == o.D && Pcap == o.Pcap && dtype == o.dtype;
+  }
+};
+
+struct ScratchSlot {
+  void* ptr = nullptr;  // device address of this device's copy of `scratch`
+  bool used = false;
+  ScratchKey key;
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+__global__ void k_take_status(unsigned* word, uint32_t* status) {
+  if (threadIdx.x == 0) {
+    *status = *word;
+    *word = 0u;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_step_noalloc(const void* q, const void* kmin_t, const void* kmax_t,
+                                      const void* k_c, const void* v_c, int B, int Hq, int Hkv,
+                                      int Lc, int D, int page_size, int r, int n_pages,
+                                      float scale, int dtype, int32_t* chan_idx,
+                                      float* page_scores, int32_t* page_idx, void* out,
+                                      uint32_t* status, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  const int P = (Lc + page_size - 1) / page_size;
+  const size_t need = step::layout(B, Hq, Hkv, D, P).total;
+  if (need > kNoAllocScratchBytes) return hipErrorInvalidValue;  // the caller checks first
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& slot = g_scratch[dev];
+  if (slot.ptr == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    slot.ptr = ptr;
+  }
+  const ScratchKey key{B * Hkv, Hq / Hkv, D, P, dtype};
+  if (!slot.used || !(slot.key == key)) {
+    // counters, status word and every tagged word start from zero for a new layout
+    e = launch_decode_ws_init(slot.ptr, need, stream);
+    if (e != hipSuccess) return e;
+    slot.used = true;
+    slot.key = key;
+  }
+  e = launch_decode_step(q, kmin_t, kmax_t, k_c, v_c, nullptr, B, Hq, Hkv, Lc, Lc, Lc, D,
+                         page_size, r, n_pages, scale, dtype, chan_idx, page_scores, page_idx, out,
+                         slot.ptr, stream);
+  if (e != hipSuccess) return e;
+  if (status != nullptr) {
+    hipLaunchKernelGGL(k_take_status, dim3(1), dim3(64), 0, stream,
+                       static_cast<unsigned*>(slot.ptr), status);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace rkv

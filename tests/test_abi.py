@@ -64,7 +64,7 @@ def test_binding_argument_types_match_header():
 
 def test_version_and_status_strings(lib):
     assert lib.rkv_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         s = lib.rkv_status_string(code)
         assert isinstance(s, bytes) and len(s) > 3
 
@@ -161,6 +161,37 @@ def test_decode_calls_reject_bad_arguments(lib):
     assert tk(FAKE, 0, 10, 3, FAKE, None, 0, None) == -2
     assert tk(FAKE, 1, 10, -1, FAKE, None, 0, None) == -2
     assert tk(None, 1, 10, 3, FAKE, None, 0, None) == -1
+
+
+def test_decode_status_and_scratch_step_reject_bad_arguments(lib):
+    st = ctypes.c_uint32(7)
+    assert lib.rkv_hybrid_decode_status(None, 4096, 0, ctypes.byref(st), None) == -1
+    assert lib.rkv_hybrid_decode_status(FAKE, 4096, 0, None, None) == -1
+    assert lib.rkv_hybrid_decode_status(FAKE, 16, 0, ctypes.byref(st), None) == -4
+    assert st.value == 7
+    na = lib.rkv_hybrid_decode_step_noalloc
+    # q kmin kmax k v, B Hq Hkv Lc D ps r n_pages, scale dtype, chan scores pages out status stream
+    base = [FAKE] * 5 + [1, 32, 8, 16384, 128, 4, 32, 128, 0.088, 1, None, None, None, FAKE,
+                         None, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return na(*a)
+
+    assert call(a0=None) == -1
+    assert call(a18=None) == -1                     # out
+    assert call(a12=4097) == -2                     # more pages than the cache has
+    assert call(a14=5) == -3
+    assert call(a9=96) == -5
+    assert call(a19=FAKE + 4) == -2                 # misaligned status word
+    # 16 x 8 = 128 KV heads of 8192 pages need more than the fixed scratch: refused before any
+    # HIP call
+    assert call(a5=16, a8=32768, a12=256) == -7
+    assert lib.rkv_status_string(-7).startswith(b"the shape needs more")
+    assert _sz(lib, "rkv_hybrid_decode_workspace_bytes", 16, 32, 8, 32768, 128, 4, 256, 1)[1] \
+        > 8 << 20
 
 
 def test_plan_budget_matches_the_oracle(lib):
