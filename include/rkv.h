@@ -194,8 +194,10 @@ int rkv_sparse_attend_decode(const void* q, const void* k_c, const void* v_c,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
- * One hybrid decode step in a single kernel launch: the approximate page scores, the page
- * top-k (k = n_pages) and the sparse attention of the three calls above ([rebuttal]
+ * One hybrid decode step: the approximate page scores, the page top-k (k = n_pages) and the
+ * sparse attention of the three calls above, in a single kernel launch when B*Hkv <= 256, and as
+ * those three calls' launches (with the scores, pages and attention partials in the workspace)
+ * when more heads than that fill the GPU with one block each ([rebuttal]
  * "Explanation of Calculating Approximate Attention Scores", "Lack of Direct Latency
  * Comparison": Steps 1-2 approximate and select, Step 3 attends). Scores and selected pages are
  * bit-identical to those of the separate calls; the output equals theirs up to float rounding
@@ -249,8 +251,10 @@ int rkv_hybrid_decode_status(void* ws, size_t ws_bytes, int clear, uint32_t* sta
  *   - The workspace is the library's own scratch: a fixed RKV_NOALLOC_SCRATCH_BYTES (8 MiB) of
  *     device memory per GPU, part of the loaded library and held until the process ends. A shape
  *     whose rkv_hybrid_decode_workspace_bytes exceeds it is refused with RKV_ERR_SCRATCH before
- *     anything is enqueued (every shape with 128 < B*Hkv <= 524000 fits, and so does any with
- *     B*Hkv*ceil(Lc/page_size) <= 2^19 pages, e.g. 8 heads of 16384-token caches at page 4).
+ *     anything is enqueued (every shape with 128 < B*Hkv <= 256 fits, and so does any with
+ *     B*Hkv <= 128 and B*Hkv*ceil(Lc/page_size) <= 2^19 pages, e.g. 8 heads of 16384-token
+ *     caches at page 4; more than 256 heads need about B*Hkv*(8*ceil(Lc/page_size) +
+ *     4*(Hq/Hkv)*(D+2)*s) bytes, s <= 8 attention splits, which 640 heads of 8192 pages exceed).
  *   - The call allocates and frees nothing. On its first call on a device it looks up that
  *     device's scratch address; whenever B*Hkv, Hq/Hkv, D, ceil(Lc/page_size) or dtype differ
  *     from the previous call's on the same device (and on the first call), it first enqueues a

@@ -22,7 +22,8 @@ struct AttendArgs {
   const void* k_c;
   const void* v_c;
   const int32_t* page_idx;  // [BH, n_pages]
-  int Lc, ps, n_pages, P, pps, nsplit;
+  const int32_t* rows;      // [BH, Lc] or null: slot t of head bh is row rows[bh*Lc + t]
+  int Lc, kv_pitch, ps, n_pages, P, pps, nsplit;  // kv_pitch: token rows per head of k_c, v_c
   float scale2;
   float* part;              // [BH, nsplit, G, D+2]
   void* out;
@@ -41,9 +42,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a) {
   __syncthreads();
   WaveState<T, D, G> st;
   st.init(static_cast<const T*>(a.q) + (size_t)bh * G * D, a.scale2);
-  st.run(static_cast<const T*>(a.k_c) + (size_t)bh * a.Lc * D,
-         static_cast<const T*>(a.v_c) + (size_t)bh * a.Lc * D, sh.pages, np_blk * a.ps, a.ps, a.P,
-         a.Lc, nullptr, 0, sh);
+  st.run(static_cast<const T*>(a.k_c) + (size_t)bh * a.kv_pitch * D,
+         static_cast<const T*>(a.v_c) + (size_t)bh * a.kv_pitch * D, sh.pages, np_blk * a.ps,
+         a.ps, a.P, a.Lc, a.rows != nullptr ? a.rows + (size_t)bh * a.Lc : nullptr,
+         a.kv_pitch - 1, sh);
   st.publish(sh);
   __syncthreads();
   T* out = static_cast<T*>(a.out);
@@ -179,18 +181,28 @@ size_t attend_ws_bytes(int B, int Hq, int Hkv, int D, int page_size, int n_pages
   return (size_t)B * Hkv * pl.nsplit * (Hq / Hkv) * (D + 2) * sizeof(float);
 }
 
-hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
-                                const int32_t* page_idx, int B, int Hq, int Hkv, int Lc, int D,
-                                int page_size, int n_pages, float scale, int dtype, void* out,
-                                void* ws, hipStream_t stream) {
+hipError_t launch_sparse_attend_view(const void* q, const void* k, const void* v,
+                                     const int32_t* rows, const int32_t* page_idx, int B, int Hq,
+                                     int Hkv, int Lc, int kv_pitch, int D, int page_size,
+                                     int n_pages, float scale, int dtype, void* out, void* ws,
+                                     hipStream_t stream) {
   const int BH = B * Hkv;
   const Plan pl = plan_attend_any(dtype, D, BH, page_size, n_pages);
-  AttendArgs a{q, k_c, v_c, page_idx, Lc, page_size, n_pages, (Lc + page_size - 1) / page_size,
-               pl.pps, pl.nsplit, scale * kLog2e, static_cast<float*>(ws), out};
+  AttendArgs a{q,        k,          v,         page_idx, rows,   Lc,
+               kv_pitch, page_size,  n_pages,   (Lc + page_size - 1) / page_size,
+               pl.pps,   pl.nsplit,  scale * kLog2e, static_cast<float*>(ws), out};
   const int G = Hq / Hkv;
   if (dtype == 0)
     return D == 64 ? attend_d<float, 64>(G, a, BH, stream) : attend_d<float, 128>(G, a, BH, stream);
   return D == 64 ? attend_d<bf16_t, 64>(G, a, BH, stream) : attend_d<bf16_t, 128>(G, a, BH, stream);
+}
+
+hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
+                                const int32_t* page_idx, int B, int Hq, int Hkv, int Lc, int D,
+                                int page_size, int n_pages, float scale, int dtype, void* out,
+                                void* ws, hipStream_t stream) {
+  return launch_sparse_attend_view(q, k_c, v_c, nullptr, page_idx, B, Hq, Hkv, Lc, Lc, D,
+                                   page_size, n_pages, scale, dtype, out, ws, stream);
 }
 
 }  // namespace rkv

@@ -22,7 +22,12 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, int BH, int Lc
                             int page_size, int dtype, void* k_c, void* v_c, void* kmin_t,
                             void* kmax_t, hipStream_t stream);
 
-// Channel selection and sign-selected page bounds.
+// Channel selection and sign-selected page bounds. The pitched form reads summary rows `pitch`
+// pages apart (pitch >= P; a cache laid out for a larger capacity) and writes rows of P scores.
+hipError_t launch_approx_scores_pitched(const void* q, const void* kmin_t, const void* kmax_t,
+                                        int B, int Hq, int Hkv, int D, int P, int pitch, int r,
+                                        int dtype, int32_t* chan_idx, float* page_scores,
+                                        hipStream_t stream);
 hipError_t launch_approx_scores(const void* q, const void* kmin_t, const void* kmax_t, int B,
                                 int Hq, int Hkv, int D, int P, int r, int dtype,
                                 int32_t* chan_idx, float* page_scores, hipStream_t stream);
@@ -46,6 +51,13 @@ hipError_t launch_sparse_attend(const void* q, const void* k_c, const void* v_c,
                                 const int32_t* page_idx, int B, int Hq, int Hkv, int Lc, int D,
                                 int page_size, int n_pages, float scale, int dtype, void* out,
                                 void* ws, hipStream_t stream);
+// The same over caches of kv_pitch token rows per head, optionally through a row map (slot t of
+// head bh is row rows[bh*Lc + t], clamped into [0, kv_pitch)).
+hipError_t launch_sparse_attend_view(const void* q, const void* k, const void* v,
+                                     const int32_t* rows, const int32_t* page_idx, int B, int Hq,
+                                     int Hkv, int Lc, int kv_pitch, int D, int page_size,
+                                     int n_pages, float scale, int dtype, void* out, void* ws,
+                                     hipStream_t stream);
 
 // One fused decode step in a single kernel: approximate page scores, page top-k, attention and
 // split merge; the blocks of a head take their roles from their block index and exchange

@@ -77,11 +77,25 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   const int Pcap = (cap + page_size - 1) / page_size;
   // laid out for the capacity, so a growing cache never moves a head's exchanged words
   const step::Layout lo = step::layout(B, Hq, Hkv, D, Pcap);
+  char* w = static_cast<char*>(ws);
+  if (lo.pipe) {
+    float* sc = page_scores != nullptr ? page_scores : reinterpret_cast<float*>(w + lo.off_pscores);
+    int32_t* pg = page_idx != nullptr ? page_idx : reinterpret_cast<int32_t*>(w + lo.off_ppages);
+    if (attend_ws_bytes(B, Hq, Hkv, D, page_size, n_pages, dtype) > lo.total - lo.off_ppart)
+      return hipErrorInvalidValue;  // cannot happen: the layout holds the largest split
+    hipError_t e = launch_approx_scores_pitched(q, kmin_t, kmax_t, B, Hq, Hkv, D, P, Pcap, r,
+                                                dtype, chan_idx, sc, stream);
+    if (e != hipSuccess) return e;
+    e = launch_topk(sc, BH, P, n_pages, pg, n_pages, nullptr, stream);
+    if (e != hipSuccess) return e;
+    return launch_sparse_attend_view(q, k_c, v_c, rows, pg, B, Hq, Hkv, Lc, kv_pitch, D,
+                                     page_size, n_pages, scale, dtype, out, w + lo.off_ppart,
+                                     stream);
+  }
   const int vmax = dtype == 0 ? vec16<float>::n : vec16<bf16_t>::n;
   const step::Plan pl = step::plan(BH, P, page_size, n_pages, device_cus(), vmax);
   if (pl.nb > 1 && (pl.ns > step::kMaxScorers || pl.na > lo.cap_a))
     return hipErrorInvalidValue;  // cannot happen: the layout holds the largest plan
-  char* w = static_cast<char*>(ws);
   step::Args a{};
   a.q = q;
   a.kmin_t = kmin_t;

@@ -447,11 +447,22 @@ inline Plan plan(int BH, int P, int ps, int n_pages, int ncu, int vmax) {
   return {ns, na, std::max(ns, na), ppb1, pps};
 }
 
+// More heads than kTargetBlocks: one block per head would leave the grid in several rounds of
+// long blocks, each running its phases one after another. Such a step runs as three launches
+// instead (page scores, top-k, attention), each spread over many short blocks, with scores, pages
+// and attention partials passing through the workspace.
+inline bool pipelined(size_t BH) { return BH > (size_t)kTargetBlocks; }
+
 // Exchange slots per head, sized for the largest plan any device can get (kTargetBlocks CUs), so
 // the layout depends on the shape only. A shape whose heads cannot get two blocks exchanges nothing.
+// A pipelined shape holds [BH, Pcap] scores, [BH, Pcap] pages and the attention partials of the
+// largest split the attention plans for n_pages <= Pcap: at most max(ceil(2*kTargetBlocks/BH),
+// ceil(Pcap/kMaxPagesPerSplit)) splits of G*(D+2) floats per head.
 struct Layout {
   size_t off_sync, off_xscores, off_xpart, total;
   int cap_a;
+  bool pipe;
+  size_t off_pscores, off_ppages, off_ppart;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -463,6 +474,18 @@ inline Layout layout(int B, int Hq, int Hkv, int D, int Pcap) {
   const int budget = BH >= (size_t)kTargetBlocks ? 0 : kTargetBlocks / (int)BH;
   lo.off_sync = 0;
   lo.off_xscores = align256((kSyncHeader + kHeadWords * BH) * sizeof(unsigned));
+  if (pipelined(BH)) {
+    const int splits = std::min(256, std::max((int)((2 * kTargetBlocks + BH - 1) / BH),
+                                              (Pcap + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit));
+    lo.cap_a = 1;
+    lo.pipe = true;
+    lo.off_xpart = lo.off_xscores;
+    lo.off_pscores = lo.off_xscores;
+    lo.off_ppages = align256(lo.off_pscores + BH * (size_t)Pcap * sizeof(float));
+    lo.off_ppart = align256(lo.off_ppages + BH * (size_t)Pcap * sizeof(int32_t));
+    lo.total = align256(lo.off_ppart + BH * (size_t)splits * G * (D + 2) * sizeof(float));
+    return lo;
+  }
   if (budget < 2) {
     lo.cap_a = 1;
     lo.off_xpart = lo.total = lo.off_xscores;

@@ -38,10 +38,21 @@ def align256(x):
     return (x + 255) & ~255
 
 
+def attend_splits_bound(BH, Pcap):
+    return min(256, max(-(-2 * TARGET // BH), -(-Pcap // MAX_PAGES_PER_WINDOW)))
+
+
 def layout(B, Hq, Hkv, D, Pcap):
     BH, G = B * Hkv, Hq // Hkv
     budget = 0 if BH >= TARGET else TARGET // BH
     lo = dict(off_sync=0, off_xscores=align256((SYNC_HEADER + HEAD_WORDS * BH) * 4))
+    if BH > TARGET:  # three launches: scores, pages and attention partials in the workspace
+        lo.update(pipe=True, cap_a=1, off_xpart=lo["off_xscores"], off_pscores=lo["off_xscores"])
+        lo["off_ppages"] = align256(lo["off_pscores"] + BH * Pcap * 4)
+        lo["off_ppart"] = align256(lo["off_ppages"] + BH * Pcap * 4)
+        lo["total"] = align256(lo["off_ppart"]
+                               + BH * attend_splits_bound(BH, Pcap) * G * (D + 2) * 4)
+        return lo
     if budget < 2:
         lo.update(cap_a=1, off_xpart=lo["off_xscores"], total=lo["off_xscores"])
         return lo
@@ -73,10 +84,67 @@ def test_layout_matches_the_library(shape):
         assert nbytes == layout(B, Hq, Hkv, D, -(-cap // ps))["total"]
 
 
+def attend_plan(BH, ps, n_pages, D, e):
+    """The standalone attention's split plan (rkv_attend.hip: plan_attend)."""
+    V = 16 // e
+    chunk = 4 * 4 * (64 // (D // V))  # waves x slots x tokens per load
+    ntok = n_pages * ps
+    ns = -(-2 * TARGET // BH)
+    ns = 1 if ntok <= SOLO_TOKENS else min(ns, -(-ntok // chunk))
+    ns = max(ns, -(-n_pages // MAX_PAGES_PER_WINDOW))
+    ns = max(min(ns, 256), 1)
+    pps = -(-n_pages // ns)
+    return -(-n_pages // pps), pps
+
+
+def approx_span(BH, P, pitch, V):
+    """Pages per block of the approximate-score launch (rkv_approx.hip: launch_g)."""
+    vec = pitch % V == 0
+    pas = 16 * (V if vec else 1)
+    span = max(1, min(8, BH * (-(-P // pas)) // 4096))
+    return pas * span, vec
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_pipelined_step_indices_stay_in_their_buffers(shape):
+    name, B, Hq, Hkv, D, Lc, pitch, ps, r, budgets, dtype = shape
+    e = 2 if dtype == "bf16" else 4
+    V = 16 // e
+    BH, G = B * Hkv, Hq // Hkv
+    if BH <= TARGET:
+        pytest.skip("one launch")
+    P = -(-Lc // ps)
+    cap = pitch if name == "grown" else Lc
+    Pcap = -(-cap // ps)
+    lo = layout(B, Hq, Hkv, D, Pcap)
+    # page scores: grid (ceil(P/per_block), BH); block bx reads pages [p0, min(P, p0+per_block))
+    # of summary rows Pcap apart, in whole vectors when Pcap is a multiple of V
+    per_block, vec = approx_span(BH, P, Pcap, V)
+    for bx in (0, -(-P // per_block) - 1):
+        p0, p1 = bx * per_block, min(P, bx * per_block + per_block)
+        last = p0 + -(-(p1 - p0) // V) * V - 1 if vec else p1 - 1
+        assert last < Pcap
+        assert (BH - 1) * D * Pcap + (D - 1) * Pcap + last < BH * D * Pcap
+        assert (BH - 1) * P + p1 - 1 < BH * Pcap  # scores, rows of P inside the [BH, Pcap] area
+    for tk in budgets:
+        n_pages = min(tk // ps, P)
+        assert (BH - 1) * n_pages + n_pages - 1 < BH * Pcap  # pages, rows of n_pages
+        ns, pps = attend_plan(BH, ps, n_pages, D, e)
+        part = 0 if ns == 1 else BH * ns * G * (D + 2) * 4
+        assert lo["off_ppart"] + part <= lo["total"]
+        assert rkv.sparse_attend_workspace_bytes(B, Hq, Hkv, D, ps, n_pages, 1 if e == 2 else 0) \
+            == part
+        # the last split's pages and the token rows they cover
+        assert (ns - 1) * pps < n_pages and ns * pps >= n_pages
+        assert (BH - 1) * pitch * D + (pitch - 1) * D + D - 1 < BH * pitch * D
+
+
 @pytest.mark.parametrize("ncu", [256, 304, 120, 8])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
 def test_fused_step_indices_stay_in_their_buffers(shape, ncu):
     name, B, Hq, Hkv, D, Lc, pitch, ps, r, budgets, dtype = shape
+    if B * Hkv > TARGET:
+        pytest.skip("three launches (see the pipelined test)")
     ncu = min(ncu, TARGET)  # the library caps the CU count at 256
     e = 2 if dtype == "bf16" else 4
     V = 16 // e  # elements per 16-byte vector
@@ -199,4 +267,7 @@ def test_library_plans_of_the_benchmarked_workloads():
     assert plan(8, 4096, 4, 512, 256, 8) == dict(ns=32, na=16, nb=32, ppb1=128, pps=32)
     assert plan(128, 1024, 4, 64, 256, 8) == dict(ns=2, na=2, nb=2, ppb1=512, pps=32)
     assert plan(640, 8192, 4, 256, 256, 8) == dict(ns=1, na=1, nb=1, ppb1=8192, pps=256)
+    # (the 80-layer stack's 640 heads run as three launches; these are their split plans)
+    assert approx_span(640, 8192, 8192, 8) == (1024, True)
+    assert attend_plan(640, 4, 256, 128, 2) == (1, 256)
     assert configs.LLAMA8B_128K.P == 4096 and configs.LLAMA70B_256K_80L.P == 8192
