@@ -35,6 +35,7 @@ struct AttendShared {
   float o[NW][G][D];
   __align__(16) float px[NW][4][32];  // per wave and row of 16 lanes: a chunk's weights (RS path)
   __align__(16) float fx[NW][4][8];   // and its per-head rescaling factors
+  __align__(16) int rowbuf[NW][32];   // MFMA path: cache rows of a wave's chunk (-1: no token)
 };
 
 // Reduce-scatter step inside a row of 16 lanes: lanes paired by the DPP pattern CTRL (an
@@ -412,6 +413,166 @@ struct WaveState {
     for (int i = 0; i < NA / 4; ++i) {
       const int f = base + i, g = f / V, e = f % V;
       sh.o[wave][g][li * V + e] = a[i];
+    }
+  }
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+// Per-wave online-softmax attention of the G <= 16 heads of a group with matrix cores (bf16,
+// D = 128), chunks of 32 tokens. v_mfma_f32_16x16x32_bf16 takes, in lane l = 16j + c (j = l/16),
+// row c of A and column c of B with the k-run of lane group j, and leaves D rows 4j..4j+3 of
+// column c. Scores: A = 16 tokens of K (row c = token, dims 32s + 8j .. +8 at k-step s), B = Q^T
+// (column c = head, the same dims; zero for heads >= G), so lane (j, c) gets tokens 4j+i of the
+// tile for head c. Over the chunk's two tiles a lane thus holds head c's scores of the 8 tokens
+// tok(j, e) = 16*(e/4) + 4j + e%4, and the weights P of those tokens are already the A operand of
+// P V (row = head c, k-run = its 8 tokens). The B operand of P V needs V[tok(j, e)][d] for one
+// column d: lane (j, c) loads the 16-byte rows V[tok(j, e)][8c .. 8c+8) and transposes them in
+// registers, so column c of output tile t is dim 8c + t and lane (j, c) ends with heads 4j..4j+3
+// of dims 8c .. 8c+8. P enters the product rounded to bf16; scores, weights and sums stay fp32.
+template <int G, int NW = kAttWaves>
+struct MfmaWave {
+  static constexpr int D = 128;
+  static_assert(G >= 1 && G <= 16, "heads of a group");
+  bf16x8_t qb[4];  // B operand of the scores, k-steps s = 0..3
+  f32x4_t o[8];    // o[t][i]: head 4j+i, dim 8c+t (unnormalised)
+  float m, l;      // head c: running max (log2 units) and this lane's part of the sum
+  float sc2;
+
+  __device__ __forceinline__ void init(const bf16_t* __restrict__ q_bh, float scale2) {
+    const int lane = threadIdx.x & (kWave - 1), j = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 raw = c < G ? load16(q_bh + (size_t)c * D + 32 * s + 8 * j) : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+    sc2 = scale2;
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Tokens [0, ntok) of the page list `pages` (LDS); this wave takes chunks wave, wave + NW, ...
+  // rows (may be null): slot t of the view is row rows[t] of kc_bh / vc_bh, clamped into
+  // [0, row_hi]. rowbuf: this wave's 32 LDS words.
+  __device__ __forceinline__ void run(const bf16_t* __restrict__ kc_bh,
+                                      const bf16_t* __restrict__ vc_bh, const int* pages,
+                                      int ntok, int ps, int P, int Lc,
+                                      const int32_t* __restrict__ rows, int row_hi,
+                                      int (&rowbuf)[32]) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int j = lane >> 4, c = lane & 15;
+    for (int c0 = wave * 32; c0 < ntok; c0 += NW * 32) {
+      if (lane < 32) {
+        const int ti = c0 + lane;
+        int row = -1;
+        if (ti < ntok) {
+          const int page = pages[ti / ps];
+          const int t = page * ps + ti % ps;
+          if (page >= 0 && page < P && t < Lc) row = rows != nullptr ? min(max(rows[t], 0), row_hi) : t;
+        }
+        rowbuf[lane] = row;
+      }
+      __builtin_amdgcn_wave_barrier();
+      // K rows of tokens c and 16 + c; V rows of tokens tok(j, e)
+      const int rk0 = rowbuf[c], rk1 = rowbuf[16 + c];
+      const int4 rv0 = *reinterpret_cast<const int4*>(&rowbuf[4 * j]);
+      const int4 rv1 = *reinterpret_cast<const int4*>(&rowbuf[16 + 4 * j]);
+      const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
+      uint4 kq[2][4], vv[8];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        kq[0][s] = load16_stream(kc_bh + (size_t)max(rk0, 0) * D + 32 * s + 8 * j);
+        kq[1][s] = load16_stream(kc_bh + (size_t)max(rk1, 0) * D + 32 * s + 8 * j);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vv[e] = load16_stream(vc_bh + (size_t)max(rv[e], 0) * D + 8 * c);
+      __builtin_amdgcn_wave_barrier();
+      // scores of head c for tokens tok(j, e), e = 4*tile + i
+      f32x4_t st[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[t][s]),
+                                                          qb[s], st[t], 0, 0, 0);
+      }
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = rv[e] >= 0 ? st[e >> 2][e & 3] * sc2 : -INFINITY;
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = xor16_step(mx, OpMax{});
+      mx = xor32_step(mx, OpMax{});
+      const float mn = fmaxf(m, mx);
+      const float f = mn == -INFINITY ? 1.f : exp2_hw(m - mn);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      f32x8_t pv;
+      float ps_sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = exp2_hw(sv[e] - mu);
+        pv[e] = pe;
+        ps_sum += pe;
+      }
+      l = l * f + ps_sum;
+      m = mn;
+      // rescale the outputs of heads 4j+i by their factors (held by lanes 4j+i); skipped when no
+      // head's max moved
+      if (__builtin_amdgcn_ballot_w64(f != 1.f) != 0ull) {
+        float fo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fo[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * j + i) * 4, __float_as_int(f)));
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[t][i] *= fo[i];
+      }
+      const bf16x8_t pa = __builtin_convertvector(pv, bf16x8_t);
+      // B operand of tile t: element t of each of the 8 V rows (dims 8c + t)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t* a = reinterpret_cast<const uint32_t*>(&vv[2 * u]);
+          const uint32_t* b = reinterpret_cast<const uint32_t*>(&vv[2 * u + 1]);
+          w[u] = __builtin_amdgcn_perm(b[t >> 1], a[t >> 1], sel);
+        }
+        const uint4 vb = make_uint4(w[0], w[1], w[2], w[3]);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb), o[t],
+                                                       0, 0, 0);
+      }
+    }
+  }
+
+  // (m, l, o) of this wave into sh, in the layout of WaveState::publish.
+  template <int DD>
+  __device__ __forceinline__ void publish(AttendShared<DD, G, NW>& sh) {
+    static_assert(DD == D, "head dim");
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int j = lane >> 4, c = lane & 15;
+    float x = l;
+    x = xor16_step(x, OpSum{});
+    x = xor32_step(x, OpSum{});
+    if (j == 0 && c < G) {
+      sh.m[wave][c] = m;
+      sh.l[wave][c] = x;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * j + i;
+      if (g < G) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) sh.o[wave][g][8 * c + t] = o[t][i];
+      }
     }
   }
 };
