@@ -29,10 +29,6 @@ struct AttendArgs {
   void* out;
 };
 
-// bf16 rows of 128 elements take the matrix-core wave (MfmaWave); other shapes the VALU wave.
-template <typename T, int D>
-constexpr bool kMatrixCores = elem<T>::bytes == 2 && D == 128;
-
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a) {
   __shared__ AttendShared<D, G> sh;
@@ -48,18 +44,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a) {
   const T* vc_bh = static_cast<const T*>(a.v_c) + (size_t)bh * a.kv_pitch * D;
   const int32_t* rows_bh = a.rows != nullptr ? a.rows + (size_t)bh * a.Lc : nullptr;
   const T* q_bh = static_cast<const T*>(a.q) + (size_t)bh * G * D;
-  if constexpr (kMatrixCores<T, D>) {
-    MfmaWave<G> st;
-    st.init(q_bh, a.scale2);
-    st.run(kc_bh, vc_bh, sh.pages, np_blk * a.ps, a.ps, a.P, a.Lc, rows_bh, a.kv_pitch - 1,
-           sh.rowbuf[tid / kWave]);
-    st.publish(sh);
-  } else {
-    WaveState<T, D, G> st;
-    st.init(q_bh, a.scale2);
-    st.run(kc_bh, vc_bh, sh.pages, np_blk * a.ps, a.ps, a.P, a.Lc, rows_bh, a.kv_pitch - 1, sh);
-    st.publish(sh);
-  }
+  AttendWave<T, D, G> st;
+  st.init(q_bh, a.scale2);
+  st.run(kc_bh, vc_bh, sh.pages, np_blk * a.ps, a.ps, a.P, a.Lc, rows_bh, a.kv_pitch - 1, sh);
+  st.publish(sh);
   __syncthreads();
   T* out = static_cast<T*>(a.out);
   for (int idx = tid; idx < G * D; idx += kAttThreads) {

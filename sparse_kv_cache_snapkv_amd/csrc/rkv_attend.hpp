@@ -441,18 +441,36 @@ struct MfmaWave {
   float m, l;      // head c: running max (log2 units) and this lane's part of the sum
   float sc2;
 
-  __device__ __forceinline__ void init(const bf16_t* __restrict__ q_bh, float scale2) {
+  // The B operand of the scores, as loaded (init(scale2) then starts a slice).
+  __device__ __forceinline__ void load_q(const bf16_t* __restrict__ q_bh) {
     const int lane = threadIdx.x & (kWave - 1), j = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint4 raw = c < G ? load16(q_bh + (size_t)c * D + 32 * s + 8 * j) : make_uint4(0, 0, 0, 0);
       qb[s] = __builtin_bit_cast(bf16x8_t, raw);
     }
+  }
+
+  __device__ __forceinline__ void init(const bf16_t* __restrict__ q_bh, float scale2) {
+    load_q(q_bh);
+    init(scale2);
+  }
+
+  __device__ __forceinline__ void init(float scale2) {
     sc2 = scale2;
     m = -INFINITY;
     l = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  template <int DD>
+  __device__ __forceinline__ void run(const bf16_t* __restrict__ kc_bh,
+                                      const bf16_t* __restrict__ vc_bh, const int* pages,
+                                      int ntok, int ps, int P, int Lc,
+                                      const int32_t* __restrict__ rows, int row_hi,
+                                      AttendShared<DD, G, NW>& sh) {
+    run(kc_bh, vc_bh, pages, ntok, ps, P, Lc, rows, row_hi, sh.rowbuf[threadIdx.x / kWave]);
   }
 
   // Tokens [0, ntok) of the page list `pages` (LDS); this wave takes chunks wave, wave + NW, ...
@@ -576,6 +594,21 @@ struct MfmaWave {
     }
   }
 };
+
+// bf16 rows of 128 elements take the matrix-core wave; other shapes the VALU wave.
+template <typename T, int D>
+constexpr bool kMatrixCores = elem<T>::bytes == 2 && D == 128;
+
+template <typename T, int D, int G, int NW, int SLOTS>
+struct AttendWaveOf {
+  using type = WaveState<T, D, G, NW, SLOTS>;
+};
+template <int G, int NW, int SLOTS>
+struct AttendWaveOf<bf16_t, 128, G, NW, SLOTS> {
+  using type = MfmaWave<G, NW>;
+};
+template <typename T, int D, int G, int NW = kAttWaves, int SLOTS = kAttSlots>
+using AttendWave = typename AttendWaveOf<T, D, G, NW, SLOTS>::type;
 
 // Combines the NW waves' (m, l, o) for output element idx = g*D + c.
 template <int D, int G, int NW = kAttWaves>
