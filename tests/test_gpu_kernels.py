@@ -184,6 +184,32 @@ def test_sparse_attend_decode(rkv, w):
         assert_rows_close(got, ref, TOL_OUT[w.dtype], f"attend n_pages={n_pages}")
 
 
+@pytest.mark.parametrize("G,ps", [(1, 1), (3, 4), (5, 2), (6, 3), (7, 4), (8, 5)])
+def test_sparse_attend_matrix_core_group_sizes(rkv, G, ps):
+    # bf16 rows of 128 go through the matrix-core wave, whose 16 columns hold the G heads and
+    # zero padding; odd page sizes and partial chunks of 32 tokens at the end of the list
+    w = configs.SMALL[1].replace(name=f"mfma-g{G}", B=2, Hq=2 * G, Hkv=2, L=1037, keep=1037,
+                                 page_size=ps, cfg_id=70 + G)
+    wc, d, qs = _cache(w, steps=1)
+    rng = np.random.default_rng(70 + G)
+    P = w.P
+    kc, vc = O.widen(d["k"]), O.widen(d["v"])
+    q = O.widen(qs[0])
+    for n_pages in sorted({1, min(P, 7), min(P, 45), P}):
+        pages = np.stack([np.stack([_random_pages(rng, P, n_pages, force_last=(b == 1))
+                                    for _ in range(w.Hkv)]) for b in range(w.B)])
+        out = rkv.rkv_sparse_attend_decode(T(qs[0]), T(d["k"]), T(d["v"]),
+                                           torch.from_numpy(pages).cuda(), ps)
+        got = O.widen(H(out))
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                toks = O.page_tokens(pages[b, h], ps, w.Lc)
+                ref = O.sparse_attention(q[b, h * G:(h + 1) * G], kc[b, h], vc[b, h], toks,
+                                         1 / math.sqrt(w.D))
+                assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT["bf16"],
+                                  f"G={G} n_pages={n_pages} b{b} h{h}")
+
+
 def test_sparse_attend_many_splits_bf16(rkv):
     # a long page list per head exercises the split + log-sum-exp merge path
     w = configs.SMALL[1].replace(name="long", B=1, Hq=8, Hkv=2, L=12500, keep=12000, cfg_id=30)
@@ -741,6 +767,63 @@ def test_mt_indexed_step_equals_step_on_gathered_cache(rkv, dtype, D, Lc, ps):
                                          1 / math.sqrt(D))
                 assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT[dtype],
                                   f"topk={topk} b{b} h{h}")
+
+
+def test_many_head_variants_run_as_three_launches(rkv):
+    # 260 KV heads (more than the 256 the single-launch step serves): the multi-turn view and the
+    # capacity layout go through the three-launch form, with their row map and pitches. Channels,
+    # scores and pages equal the plain step on gathered / dense copies bit for bit, and sampled
+    # heads match the oracle.
+    B, Hq, Hkv, D, L, Lc, ps, r = 130, 8, 2, 128, 1500, 333, 4, 32
+    dt = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(37)
+    k, v = _randn((B, Hkv, L, D), g, dt), _randn((B, Hkv, L, D), g, dt)
+    kept = torch.sort(torch.rand((B, Hkv, L), device="cuda", generator=g).argsort(-1)[..., :Lc],
+                      -1).values.to(torch.int32).contiguous()
+    bi = torch.arange(B, device="cuda")[:, None, None]
+    hi = torch.arange(Hkv, device="cuda")[None, :, None]
+    kg, vg = k[bi, hi, kept.long()].contiguous(), v[bi, hi, kept.long()].contiguous()
+    kmin, kmax = rkv.rkv_build_page_summaries_indexed(k, kept, ps)
+    gmin, gmax = rkv.rkv_build_page_summaries(kg, ps)
+    P = kmin.shape[-1]
+    # a capacity layout holding the gathered cache in its first Lc of cap slots
+    cap = 400
+    kc = torch.zeros((B, Hkv, cap, D), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[:, :, :Lc] = kg
+    vc[:, :, :Lc] = vg
+    cmin, cmax = rkv.rkv_build_page_summaries_cap(kc, Lc, ps)
+    q64s = []
+    for n_pages in (16, 60):
+        q = _randn((B, Hq, D), g, dt)
+        res = []
+        for fn, args in ((rkv.rkv_hybrid_decode_step_indexed, (q, kmin, kmax, k, v, kept)),
+                         (rkv.rkv_hybrid_decode_step, (q, gmin, gmax, kg, vg))):
+            chans = torch.empty((B, Hkv, r), dtype=torch.int32, device="cuda")
+            scores = torch.empty((B, Hkv, P), dtype=torch.float32, device="cuda")
+            pages = torch.empty((B, Hkv, n_pages), dtype=torch.int32, device="cuda")
+            out = fn(*args, ps, r, n_pages, chan_idx=chans, page_scores=scores, page_idx=pages)
+            res.append((chans, scores, pages, out))
+        chans = torch.empty((B, Hkv, r), dtype=torch.int32, device="cuda")
+        scores = torch.empty((B, Hkv, P), dtype=torch.float32, device="cuda")
+        pages = torch.empty((B, Hkv, n_pages), dtype=torch.int32, device="cuda")
+        out = rkv.rkv_hybrid_decode_step_cap(q, cmin, cmax, kc, vc, Lc, ps, r, n_pages,
+                                             chan_idx=chans, page_scores=scores, page_idx=pages)
+        res.append((chans, scores, pages, out))
+        torch.cuda.synchronize()
+        (c1, s1, p1, o1) = res[1]
+        for c2, s2, p2, o2 in (res[0], res[2]):
+            assert torch.equal(c1, c2) and torch.equal(p1, p2), f"n_pages={n_pages}"
+            assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        got, pg, q64 = O.widen(H(o1)), p1.cpu().numpy(), O.widen(H(q))
+        G = Hq // Hkv
+        for b, h in ((0, 0), (64, 1), (B - 1, Hkv - 1)):
+            toks = O.page_tokens(pg[b, h], ps, Lc)
+            ref = O.sparse_attention(q64[b, h * G:(h + 1) * G], O.widen(H(kg[b, h])),
+                                     O.widen(H(vg[b, h])), toks, 1 / math.sqrt(D))
+            assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT["bf16"],
+                              f"n_pages={n_pages} b{b} h{h}")
 
 
 # ----------------------------------------------------------------------------- selection quality
