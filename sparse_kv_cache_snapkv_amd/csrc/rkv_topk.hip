@@ -22,16 +22,17 @@ namespace {
 
 constexpr int kBlockThreads = 256;
 
-template <int E>
-__global__ __launch_bounds__(kBlockThreads) void k_topk_block(const float* __restrict__ scores,
-                                                             int n, int k,
-                                                             int32_t* __restrict__ out,
-                                                             int out_stride) {
-  __shared__ SelectShared<kBlockThreads> sh;
+// One block per row, E keys per thread; rows of up to 4096 keys take 256 threads, longer ones
+// (up to 8192) 512, which halves the keys each thread ranks and compacts.
+template <int THREADS, int E>
+__global__ __launch_bounds__(THREADS) void k_topk_block(const float* __restrict__ scores, int n,
+                                                       int k, int32_t* __restrict__ out,
+                                                       int out_stride) {
+  __shared__ SelectShared<THREADS> sh;
   const float* row = scores + (size_t)blockIdx.x * n;
   int32_t* o = out + (size_t)blockIdx.x * out_stride;
   if (k >= n) {
-    for (int i = threadIdx.x; i < n; i += kBlockThreads) o[i] = i;
+    for (int i = threadIdx.x; i < n; i += THREADS) o[i] = i;
     return;
   }
   if (k <= 0) return;
@@ -39,11 +40,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk_block(const float* __res
   const int i0 = threadIdx.x * E;
   const int nv = load_keys<E>(row, n, i0, key);
   uint32_t T, need_eq;
-  block_threshold<kBlockThreads, E>(key, nv, (uint32_t)k, T, need_eq, sh);
-  block_compact<kBlockThreads, E>(key, nv, T, need_eq, i0, 0u, (uint32_t)k, sh,
-                                  [&](uint32_t pos, int idx, bool take) {
-                                    if (take && pos < (uint32_t)k) o[pos] = idx;
-                                  });
+  block_threshold<THREADS, E>(key, nv, (uint32_t)k, T, need_eq, sh);
+  block_compact<THREADS, E>(key, nv, T, need_eq, i0, 0u, (uint32_t)k, sh,
+                            [&](uint32_t pos, int idx, bool take) {
+                              if (take && pos < (uint32_t)k) o[pos] = idx;
+                            });
 }
 
 // ------------------------------------------------------------------------------ long rows
@@ -291,13 +292,13 @@ hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out
                        void* ws, hipStream_t stream) {
   dim3 grid(rows);
   if (n <= 16 * kBlockThreads) {
-    hipLaunchKernelGGL(k_topk_block<16>, grid, dim3(kBlockThreads), 0, stream, scores, n, k, out,
-                       out_stride);
+    hipLaunchKernelGGL((k_topk_block<kBlockThreads, 16>), grid, dim3(kBlockThreads), 0, stream,
+                       scores, n, k, out, out_stride);
     return hipGetLastError();
   }
   if (n <= 32 * kBlockThreads) {
-    hipLaunchKernelGGL(k_topk_block<32>, grid, dim3(kBlockThreads), 0, stream, scores, n, k, out,
-                       out_stride);
+    hipLaunchKernelGGL((k_topk_block<2 * kBlockThreads, 16>), grid, dim3(2 * kBlockThreads), 0,
+                       stream, scores, n, k, out, out_stride);
     return hipGetLastError();
   }
   if (k <= 0) return hipSuccess;
