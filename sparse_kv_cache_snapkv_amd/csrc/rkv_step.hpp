@@ -39,7 +39,7 @@ namespace step {
 constexpr int kThreads = 512;  // two waves per SIMD
 constexpr int kWaves = kThreads / kWave;
 constexpr int kSlots = 4;            // row loads per wave per chunk of attention
-constexpr int kSoloTokens = 128;     // budgets up to this many tokens: one attender per head
+constexpr int kSoloTokens = 256;     // budgets up to this many tokens: one attender per head
 constexpr int kTokensPerBlock = 64;  // otherwise one attender per this many budget tokens,
 constexpr int kMaxAttending = 16;    // at most this many per head
 constexpr int kMaxScorers = 64;

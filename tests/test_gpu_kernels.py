@@ -443,7 +443,7 @@ def test_limits_at_their_maximum(rkv):
 PLAN_CASES = [
     # name, dtype, B, Hq, Hkv, D, P, ps, top-k budgets
     ("bh8-p4096", "bf16", 1, 32, 8, 128, 4096, 4, (128, 512, 1024, 2048)),
-    ("bh128-p1024", "bf16", 16, 32, 8, 128, 1024, 4, (256, 64)),
+    ("bh128-p1024", "bf16", 16, 32, 8, 128, 1024, 4, (256, 64, 1024)),
     ("bh9-ragged", "bf16", 3, 12, 3, 64, 777, 3, (3, 300, 1500)),
     ("g8-bh1", "bf16", 1, 8, 1, 128, 2000, 2, (1200, 130)),
     ("fp32-bh4", "fp32", 2, 4, 2, 64, 500, 2, (200, 998)),
@@ -544,7 +544,7 @@ def test_fused_decode_step_stealing(rkv, case, monkeypatch):
             assert_rows_close(got[b, h * G:(h + 1) * G], ref, TOL_OUT[dtype], f"{name} k{topk}")
     # informational bits: 16 = an attender scored a share, 32 = an attender attended a slice
     assert stole & 16, "no share was scored by an attender"
-    assert stole & 32 or all(min(tk // ps, P) * ps <= 128 for tk in budgets), "no slice redone"
+    assert stole & 32 or all(min(tk // ps, P) * ps <= 256 for tk in budgets), "no slice redone"
 
 
 def _tied_keys(B, Hkv, P, ps, D, mode, seed):

@@ -17,7 +17,7 @@ from workloads import configs
 
 THREADS = 512
 MAX_ATT, MAX_SCORE, TARGET = 16, 64, 256
-SOLO_TOKENS, TOKENS_PER_BLOCK = 128, 64
+SOLO_TOKENS, TOKENS_PER_BLOCK = 256, 64
 SYNC_HEADER, HEAD_WORDS = 16, 4
 MAX_PAGES_PER_WINDOW = 1024
 
@@ -265,7 +265,7 @@ def test_library_plans_of_the_benchmarked_workloads():
     assert plan(8, 4096, 4, 32, 256, 8) == dict(ns=32, na=1, nb=32, ppb1=128, pps=32)
     assert plan(8, 4096, 4, 128, 256, 8) == dict(ns=32, na=8, nb=32, ppb1=128, pps=16)
     assert plan(8, 4096, 4, 512, 256, 8) == dict(ns=32, na=16, nb=32, ppb1=128, pps=32)
-    assert plan(128, 1024, 4, 64, 256, 8) == dict(ns=2, na=2, nb=2, ppb1=512, pps=32)
+    assert plan(128, 1024, 4, 64, 256, 8) == dict(ns=2, na=1, nb=2, ppb1=512, pps=64)
     assert plan(640, 8192, 4, 256, 256, 8) == dict(ns=1, na=1, nb=1, ppb1=8192, pps=256)
     # (the 80-layer stack's 640 heads run as three launches; these are their split plans)
     assert approx_span(640, 8192, 8192, 8) == (1024, True)
