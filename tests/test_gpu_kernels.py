@@ -448,6 +448,10 @@ PLAN_CASES = [
     ("g8-bh1", "bf16", 1, 8, 1, 128, 2000, 2, (1200, 130)),
     ("fp32-bh4", "fp32", 2, 4, 2, 64, 500, 2, (200, 998)),
     ("bh320-solo", "bf16", 40, 32, 8, 64, 300, 4, (512,)),
+    # over 256 heads (the three-launch form): fp32 rows on the VALU attention wave, and bf16 rows
+    # of 128 on the matrix-core wave with a top-k row of more than 4096 pages (512-thread rows)
+    ("bh264-fp32", "fp32", 66, 8, 4, 64, 700, 2, (64, 1400)),
+    ("bh264-p5000", "bf16", 33, 64, 8, 128, 5000, 1, (700, 5000)),
 ]
 
 
@@ -478,8 +482,8 @@ def test_fused_decode_step_plans(rkv, case):
 
 
 def test_fused_decode_step_beside_a_busy_stream(rkv):
-    # The blocks of a head take their roles from tickets and only wait for blocks that started
-    # before them, so fused steps finish with correct results while another stream's kernels
+    # A block that still misses another block's scores or slice at the steal deadline does that
+    # work itself, so fused steps finish with correct results while another stream's kernels
     # hold CUs at the same time. The outputs equal those of the same steps run alone.
     w = configs.SMALL[1].replace(name="busy", B=1, Hq=32, Hkv=8, D=128, L=8192, keep=8192,
                                  page_size=4, r=32, cfg_id=46)
