@@ -584,8 +584,14 @@ def test_fused_decode_step_tied_scores(rkv, mode, B, P):
         _check_fused_heads(rkv, w, q, k_c, v_c, n * ps, heads, 1 / math.sqrt(D))
 
 
-def test_fused_decode_step_graph_replays(rkv):
-    w = configs.SMALL[1]
+GRAPH_CASES = [configs.SMALL[1],
+               # 264 heads: the step's three launches (scores, top-k, attention) in one graph
+               configs.SMALL[1].replace(name="graph-264-heads", B=132, L=600, keep=600, W=16,
+                                        n_needles=2, cfg_id=48)]
+
+
+@pytest.mark.parametrize("w", GRAPH_CASES, ids=_wid)
+def test_fused_decode_step_graph_replays(rkv, w):
     wc, d, qs = _cache(w, steps=3)
     kc_t, vc_t = T(d["k"]), T(d["v"])
     kmin, kmax = rkv.rkv_build_page_summaries(kc_t, w.page_size)
