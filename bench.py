@@ -51,10 +51,10 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str) -> None:
-    """Per-launch HBM traffic of the dominant kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
-    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for the plain
-    256 MiB device copy the run starts with (known bytes / counted bytes)."""
+def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, kernel: str = DOMINANT) -> None:
+    """Per-launch HBM traffic of a kernel (by default the dominant one) from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads
+    for the plain 256 MiB device copy the run starts with (known bytes / counted bytes)."""
     import csv
 
     def dispatches(path, counter):
@@ -64,14 +64,14 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str) -> None:
                 rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
         return sorted(rows)
 
-    out = dict(sources_sha256=kernel_sources_digest(), kernel=DOMINANT,
+    out = dict(sources_sha256=kernel_sources_digest(), kernel=kernel,
                copy_bytes=COPY_CALIBRATION_BYTES)
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = dispatches(path, counter)
         # the calibration copy is the run's first copy kernel (inputs are drawn after it)
         copy = next(v for _, name, v in rows if "copy" in name)
         factor = COPY_CALIBRATION_BYTES / (copy * 1024.0)
-        dom = [v for _, name, v in rows if DOMINANT in name]
+        dom = [v for _, name, v in rows if kernel in name]
         out[counter] = dict(copy_kib=copy, factor=factor, launches=len(dom),
                             mean_kib_per_launch=sum(dom) / len(dom),
                             scaled_bytes_per_launch=sum(dom) / len(dom) * 1024.0 * factor)
@@ -250,7 +250,9 @@ def layers80_decode(rkv, torch, reps: int) -> dict:
     from workloads import configs, runs
     w = configs.LLAMA70B_256K_80L
     L = w.layers
-    st = runs.compressed_stack(rkv, w, L)
+    st = runs.compressed_stack(rkv, w, L,
+                               on_layer=lambda i: progress(f"layers80: layer {i} evicted")
+                               if i % 10 == 9 else None)
     kmin, kmax = rkv.rkv_build_page_summaries(st["k_c"], w.page_size)
     wl = w.replace(B=L * w.B)
     res = decode_rows(rkv, torch, wl, st["k_c"], st["v_c"], kmin, kmax, 1, w.steps, reps)
@@ -345,6 +347,29 @@ def cpu_baseline(w_main, sample_steps: int) -> dict:
                 per_config=per_config)
 
 
+def calibration_copy(torch, dev) -> None:
+    """A plain device copy of COPY_CALIBRATION_BYTES, the counters' scale."""
+    src = torch.ones(COPY_CALIBRATION_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _other_workloads():
+    from workloads import configs
+    return {
+        "tiny": lambda rkv, torch, reps: small_decode(rkv, torch, configs.TINY_FP32, reps),
+        "llama8b_32k": lambda rkv, torch, reps: small_decode(rkv, torch, configs.LLAMA8B_32K, reps),
+        "batch16": lambda rkv, torch, reps: batch16_decode(rkv, torch, 4, reps),
+        "layers80": lambda rkv, torch, reps: layers80_decode(rkv, torch, reps),
+        "evict_70b_layer": lambda rkv, torch, reps: evict_70b_layer(rkv, torch),
+    }
+
+
+OTHER_WORKLOADS = _other_workloads()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,9 +386,13 @@ def main() -> int:
                     help="start with a plain 256 MiB device copy (the counters' scale)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="write the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-kernel", default=DOMINANT,
+                    help="kernel-name substring whose launches --pmc-summary averages")
+    ap.add_argument("--only", choices=sorted(OTHER_WORKLOADS),
+                    help="run only this other workload's section and print its JSON (profiling)")
     args = ap.parse_args()
     if args.pmc_summary:
-        summarize_pmc(*args.pmc_summary)
+        summarize_pmc(*args.pmc_summary, kernel=args.pmc_kernel)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the RocketKV path here runs on a single MI355X "
@@ -378,6 +407,11 @@ def main() -> int:
     w = configs.by_name(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        if args.pmc_calibration:
+            calibration_copy(torch, dev)
+        print(json.dumps({args.only: OTHER_WORKLOADS[args.only](rkv, torch, 5)}), flush=True)
+        return 0
     R = args.replicas
     nsteps = args.decode_steps or w.steps
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -387,11 +421,7 @@ def main() -> int:
     reps = 5
 
     if args.pmc_calibration:
-        src = torch.ones(COPY_CALIBRATION_BYTES // 2, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch, dev)
 
     # ---- inputs resident in HBM, outputs and workspaces preallocated. Everything runs on the
     # current (default) stream: each stage is run once eagerly, then captured as a HIP graph.
@@ -650,13 +680,9 @@ def extra(rkv, torch, gen, w, line, prompts, kept, k_c, v_c, kmin, kmax, q_dec, 
     # 80-layer 70B-shaped stack, and one 70B-shaped layer's eviction
     torch.cuda.empty_cache()
     other = {}
-    for name, fn in (("tiny", lambda: small_decode(rkv, torch, configs.TINY_FP32, reps)),
-                     ("llama8b_32k", lambda: small_decode(rkv, torch, configs.LLAMA8B_32K, reps)),
-                     ("batch16", lambda: batch16_decode(rkv, torch, 4, reps)),
-                     ("layers80", lambda: layers80_decode(rkv, torch, reps)),
-                     ("evict_70b_layer", lambda: evict_70b_layer(rkv, torch))):
+    for name in ("tiny", "llama8b_32k", "batch16", "layers80", "evict_70b_layer"):
         progress(name)
-        other[name] = fn()
+        other[name] = OTHER_WORKLOADS[name](rkv, torch, reps)
         torch.cuda.empty_cache()
     line["other_workloads"] = other
     torch.cuda.empty_cache()

@@ -19,8 +19,9 @@ def _dtype(w: Workload):
     return torch.float32 if w.dtype == "fp32" else torch.bfloat16
 
 
-def compressed_stack(rkv, w: Workload, layers: int, sample=(), device="cuda"):
-    """Evicts `layers` independently drawn layers. Returns dict with
+def compressed_stack(rkv, w: Workload, layers: int, sample=(), device="cuda", on_layer=None):
+    """Evicts `layers` independently drawn layers (on_layer(layer), if given, after each one).
+    Returns dict with
     k_c, v_c [layers*B, Hkv, Lc, D], kept [layers*B, Hkv, Lc] int32,
     needles_ok (bool: every planted needle survived in every head) and
     host: {(layer, b, h): dict(q_win [G,W,D], k [L,D], v [L,D], needle_pos)} storage arrays."""
@@ -49,4 +50,6 @@ def compressed_stack(rkv, w: Workload, layers: int, sample=(), device="cuda"):
             hit = (kept[sl_].unsqueeze(-1).long() == d["needle_pos"].unsqueeze(-2)).any(dim=-2)
             needles_ok = needles_ok and bool(hit.all())
         del d
+        if on_layer is not None:
+            on_layer(layer)
     return dict(k_c=k_c, v_c=v_c, kept=kept, needles_ok=needles_ok, host=host)
