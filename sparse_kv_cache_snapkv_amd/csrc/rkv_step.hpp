@@ -43,6 +43,9 @@ constexpr int kSoloTokens = 256;     // budgets up to this many tokens: one atte
 constexpr int kTokensPerBlock = 64;  // otherwise one attender per this many budget tokens,
 constexpr int kMaxAttending = 16;    // at most this many per head
 constexpr int kMaxScorers = 64;
+// A score share never has fewer pages than this: a head of few pages is scored by few blocks
+// (one for 128 pages, with no exchange at all), as each share costs a full exchange round trip.
+constexpr int kMinScorePages = 128;
 constexpr int kTargetBlocks = 256;   // CUs of an MI355X: the grid of a waiting plan fits them
 constexpr int kSyncHeader = 16;      // words before the per-head words; word 0 is the status
 constexpr int kHeadWords = 4;        // per head: epoch, started count, two spare
@@ -441,7 +444,7 @@ inline Plan plan(int BH, int P, int ps, int n_pages, int ncu, int vmax) {
                           1);
   const int pps = (n_pages + na - 1) / na;
   na = (n_pages + pps - 1) / pps;
-  int ppb1 = (P + nb0 - 1) / nb0;
+  int ppb1 = std::max((P + nb0 - 1) / nb0, kMinScorePages);
   ppb1 = (ppb1 + vmax - 1) / vmax * vmax;
   const int ns = (P + ppb1 - 1) / ppb1;
   return {ns, na, std::max(ns, na), ppb1, pps};

@@ -20,6 +20,7 @@ MAX_ATT, MAX_SCORE, TARGET = 16, 64, 256
 SOLO_TOKENS, TOKENS_PER_BLOCK = 256, 64
 SYNC_HEADER, HEAD_WORDS = 16, 4
 MAX_PAGES_PER_WINDOW = 1024
+MIN_SCORE_PAGES = 128
 
 
 def plan(BH, P, ps, n_pages, ncu, vmax):
@@ -28,7 +29,7 @@ def plan(BH, P, ps, n_pages, ncu, vmax):
     na = 1 if ntok <= SOLO_TOKENS else max(min(MAX_ATT, nb0, -(-ntok // TOKENS_PER_BLOCK)), 1)
     pps = -(-n_pages // na)
     na = -(-n_pages // pps)
-    ppb1 = -(-P // nb0)
+    ppb1 = max(-(-P // nb0), MIN_SCORE_PAGES)
     ppb1 = -(-ppb1 // vmax) * vmax
     ns = -(-P // ppb1)
     return dict(ns=ns, na=na, nb=max(ns, na), ppb1=ppb1, pps=pps)
@@ -270,4 +271,7 @@ def test_library_plans_of_the_benchmarked_workloads():
     # (the 80-layer stack's 640 heads run as three launches; these are their split plans)
     assert approx_span(640, 8192, 8192, 8) == (1024, True)
     assert attend_plan(640, 4, 256, 128, 2) == (1, 256)
+    # the 2K fp32 workload's two heads of 128 pages: one block per head, nothing exchanged
+    assert plan(2, 128, 4, 32, 256, 4) == dict(ns=1, na=1, nb=1, ppb1=128, pps=32)
+    assert plan(8, 1024, 4, 32, 256, 8) == dict(ns=8, na=1, nb=8, ppb1=128, pps=32)
     assert configs.LLAMA8B_128K.P == 4096 and configs.LLAMA70B_256K_80L.P == 8192
