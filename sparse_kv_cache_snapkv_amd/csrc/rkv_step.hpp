@@ -21,7 +21,9 @@
 // end, so the count's round trip delays nobody) stores the new epoch and clears the count: by
 // then every block of the head has read the old epoch, and no block of the call reads it again.
 //
-// One-block heads (large B*Hkv: nb = 1) score into LDS and exchange nothing.
+// One-block heads (nb = 1: heads of at most 128 pages, or more heads than fit two blocks each)
+// score into LDS and exchange nothing. Over kTargetBlocks heads the step does not use this kernel
+// (pipelined(): the scoring, top-k and attention kernels of the separate calls, in turn).
 #pragma once
 
 #include <math.h>
