@@ -596,9 +596,6 @@ struct MfmaWave {
 };
 
 // bf16 rows of 128 elements take the matrix-core wave; other shapes the VALU wave.
-template <typename T, int D>
-constexpr bool kMatrixCores = elem<T>::bytes == 2 && D == 128;
-
 template <typename T, int D, int G, int NW, int SLOTS>
 struct AttendWaveOf {
   using type = WaveState<T, D, G, NW, SLOTS>;

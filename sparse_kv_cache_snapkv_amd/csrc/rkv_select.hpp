@@ -362,44 +362,36 @@ __device__ __forceinline__ void strided_clear(StridedShared<THREADS, E>& sh) {
 // valid keys, with sh cleared by strided_clear (and a barrier passed) since its last use.
 // Value-linear bins between the block's minimum and maximum locate the bin of the k-th largest
 // key; a bin of at most kStridedCandidates keys is gathered and ranked, larger ones (clustered
-// values) go to block_threshold's radix passes in fb. Every thread must call it. With
-// extremes_given, lo_given / hi_given are the smallest and largest valid key (block-uniform), and
-// the block reduction that would find them is skipped.
+// values) go to block_threshold's radix passes in fb. Every thread must call it.
 template <int THREADS, int E>
 __device__ __forceinline__ void strided_threshold(const uint32_t (&key)[E], int nvalid, uint32_t k,
                                                   uint32_t& T, uint32_t& need_eq,
                                                   uint32_t& eq_total,
                                                   StridedShared<THREADS, E>& sh,
-                                                  SelectShared<THREADS>& fb,
-                                                  bool extremes_given = false,
-                                                  uint32_t lo_given = 0u, uint32_t hi_given = 0u) {
+                                                  SelectShared<THREADS>& fb) {
   constexpr int NW = THREADS / kWave;
   constexpr int BPT = kValueBins / THREADS;
   static_assert(BPT % 4 == 0, "bins per thread");
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
-  uint32_t lo = lo_given, hi = hi_given;
-  if (!extremes_given) {
-    lo = 0xffffffffu;
-    hi = 0u;
+  uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      lo = e < nvalid ? min(lo, key[e]) : lo;
-      hi = e < nvalid ? max(hi, key[e]) : hi;
-    }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    if (lane == 0) {
-      sh.wmin[wave] = lo;
-      sh.wmax[wave] = hi;
-    }
-    lds_barrier();
-    lo = sh.wmin[0];
-    hi = sh.wmax[0];
+  for (int e = 0; e < E; ++e) {
+    lo = e < nvalid ? min(lo, key[e]) : lo;
+    hi = e < nvalid ? max(hi, key[e]) : hi;
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    sh.wmin[wave] = lo;
+    sh.wmax[wave] = hi;
+  }
+  lds_barrier();
+  lo = sh.wmin[0];
+  hi = sh.wmax[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      lo = min(lo, sh.wmin[w]);
-      hi = max(hi, sh.wmax[w]);
-    }
+  for (int w = 1; w < NW; ++w) {
+    lo = min(lo, sh.wmin[w]);
+    hi = max(hi, sh.wmax[w]);
   }
   if (lo == hi) {  // all keys equal
     T = lo;
