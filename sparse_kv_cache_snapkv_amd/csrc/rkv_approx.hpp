@@ -15,18 +15,19 @@ struct ChannelShared {
   float qc[kApproxMaxD];  // sum_g q_g of the j-th chosen channel
   __align__(16) uint64_t key[kApproxMaxD];  // {sum |q| bits, 127 - channel}: distinct, ordered
   float qb[kApproxMaxD];
-  unsigned rank[2][kApproxMaxD];            // partial ranks over the two halves of the channels
+  unsigned rank[4][kApproxMaxD];            // partial ranks over 2 or 4 parts of the channels
 };
 
 // Chooses the r channels with the largest sum_g |q_g[c]| of group (b, h) (ties: lower channel)
 // and lists them ascending in sh.chan, with sum_g q_g[c] in sh.qc. Both sums run over g in
 // ascending order. Each channel gets a distinct 64-bit key (the sum's bits, which order like the
 // value for non-negative floats, above 127 - c, so equal sums rank the lower channel higher);
-// thread t counts the keys of channels [64*(t/128), 64*(t/128) + 64) above channel t % 128's
-// key, and the two halves add up to its rank. Wave 0 then places the channels of rank < r in
-// ascending channel order by ballot prefix counts. The block must have at least 256 threads and
-// every thread must take every step: load, then phase 1 (which ends with a barrier), then phase 2
-// (two barriers). The load is separate so that a kernel can issue its other first loads before
+// the keys split into PARTS parts (2 of 64, or 4 of 32 for a block of 512 threads, which halves
+// each thread's chain of LDS reads), thread t counts the keys of part t / 128 above channel
+// t % 128's key, and the parts add up to its rank. Wave 0 then places the channels of rank < r
+// in ascending channel order by ballot prefix counts. The block must have at least 128 * PARTS
+// threads and every thread must take every step: load, then phase 1 (which ends with a
+// barrier), then phase 2 (two barriers). The load is separate so that a kernel can issue its other first loads before
 // any of them is waited for.
 template <typename T, int G>
 struct ChannelQ {
@@ -64,27 +65,34 @@ struct NoHook {
 
 // before_last_barrier() runs (in every thread) just before the final barrier, so that what it
 // writes to LDS is visible to the whole block on return.
-template <typename Hook = NoHook>
+template <int PARTS = 2, typename Hook = NoHook>
 __device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShared& sh,
                                                        Hook&& before_last_barrier = Hook{}) {
+  static_assert(PARTS == 2 || PARTS == 4, "parts of the keys");
+  constexpr int PK = kApproxMaxD / PARTS;  // keys per part
   const int tid = threadIdx.x;
-  if (tid < 2 * kApproxMaxD) {
-    const int c = tid % kApproxMaxD, half = tid / kApproxMaxD;
+  if (tid < PARTS * kApproxMaxD) {
+    const int c = tid % kApproxMaxD, part = tid / kApproxMaxD;
     const uint64_t kc = sh.key[c];
     unsigned above = 0;
 #pragma unroll
-    for (int j = 0; j < kApproxMaxD / 2; j += 2) {
-      const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(&sh.key[half * 64 + j]);
+    for (int j = 0; j < PK; j += 2) {
+      const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(&sh.key[part * PK + j]);
       above += (kk.x > kc) + (kk.y > kc);
     }
-    sh.rank[half][c] = above;
+    sh.rank[part][c] = above;
   }
   lds_barrier();
   if (tid < kWave) {
     const int lane = tid;
-    const bool t0 = lane < D && sh.rank[0][lane] + sh.rank[1][lane] < (unsigned)r;
-    const bool t1 = lane + kWave < D &&
-                    sh.rank[0][lane + kWave] + sh.rank[1][lane + kWave] < (unsigned)r;
+    unsigned r0 = 0, r1 = 0;
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) {
+      r0 += sh.rank[q][lane];
+      r1 += sh.rank[q][lane + kWave];
+    }
+    const bool t0 = lane < D && r0 < (unsigned)r;
+    const bool t1 = lane + kWave < D && r1 < (unsigned)r;
     const uint64_t b0 = __ballot(t0), b1 = __ballot(t1);
     const uint64_t below = (1ull << lane) - 1ull;
     if (t0) {
