@@ -15,19 +15,20 @@ struct ChannelShared {
   float qc[kApproxMaxD];  // sum_g q_g of the j-th chosen channel
   __align__(16) uint64_t key[kApproxMaxD];  // {sum |q| bits, 127 - channel}: distinct, ordered
   float qb[kApproxMaxD];
-  unsigned rank[4][kApproxMaxD];            // partial ranks over 2 or 4 parts of the channels
+  unsigned rank[8][kApproxMaxD];            // partial ranks over the parts of the keys
 };
 
 // Chooses the r channels with the largest sum_g |q_g[c]| of group (b, h) (ties: lower channel)
 // and lists them ascending in sh.chan, with sum_g q_g[c] in sh.qc. Both sums run over g in
 // ascending order. Each channel gets a distinct 64-bit key (the sum's bits, which order like the
 // value for non-negative floats, above 127 - c, so equal sums rank the lower channel higher);
-// the keys split into PARTS parts (2 of 64, or 4 of 32 for a block of 512 threads, which halves
-// each thread's chain of LDS reads), thread t counts the keys of part t / 128 above channel
-// t % 128's key, and the parts add up to its rank. Wave 0 then places the channels of rank < r
-// in ascending channel order by ballot prefix counts. The block must have at least 128 * PARTS
-// threads and every thread must take every step: load, then phase 1 (which ends with a
-// barrier), then phase 2 (two barriers). The load is separate so that a kernel can issue its other first loads before
+// the keys split into PARTS parts and each of the block's THREADS threads counts, for
+// 128 * PARTS / THREADS channels, the keys of one part above that channel's key (more parts, a
+// shorter chain of LDS reads per thread: 16 keys each with 8 parts in 512 threads, 32 with 4 in
+// 256); the parts add up to each channel's rank. Wave 0 then places the channels of rank < r in
+// ascending channel order by ballot prefix counts. The block must have exactly THREADS threads
+// and every thread must take every step: load, then phase 1 (which ends with a barrier), then
+// phase 2 (two barriers). The load is separate so that a kernel can issue its other first loads before
 // any of them is waited for.
 template <typename T, int G>
 struct ChannelQ {
@@ -65,23 +66,31 @@ struct NoHook {
 
 // before_last_barrier() runs (in every thread) just before the final barrier, so that what it
 // writes to LDS is visible to the whole block on return.
-template <int PARTS = 2, typename Hook = NoHook>
+template <int PARTS = 2, int THREADS = 256, typename Hook = NoHook>
 __device__ __forceinline__ void select_channels_phase2(int D, int r, ChannelShared& sh,
                                                        Hook&& before_last_barrier = Hook{}) {
-  static_assert(PARTS == 2 || PARTS == 4, "parts of the keys");
-  constexpr int PK = kApproxMaxD / PARTS;  // keys per part
+  static_assert(PARTS >= 2 && PARTS <= 8 && kApproxMaxD % PARTS == 0, "parts of the keys");
+  constexpr int PK = kApproxMaxD / PARTS;             // keys per part
+  constexpr int CPT = kApproxMaxD * PARTS / THREADS;  // channels per thread
+  constexpr int CS = kApproxMaxD / CPT;               // stride between a thread's channels
+  static_assert(CPT >= 1 && CPT * THREADS == kApproxMaxD * PARTS, "threads per part");
   const int tid = threadIdx.x;
-  if (tid < PARTS * kApproxMaxD) {
-    const int c = tid % kApproxMaxD, part = tid / kApproxMaxD;
-    const uint64_t kc = sh.key[c];
-    unsigned above = 0;
+  const int part = tid / CS, c0 = tid % CS;
+  uint64_t kc[CPT];
+  unsigned above[CPT];
 #pragma unroll
-    for (int j = 0; j < PK; j += 2) {
-      const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(&sh.key[part * PK + j]);
-      above += (kk.x > kc) + (kk.y > kc);
-    }
-    sh.rank[part][c] = above;
+  for (int i = 0; i < CPT; ++i) {
+    kc[i] = sh.key[c0 + i * CS];
+    above[i] = 0u;
   }
+#pragma unroll
+  for (int j = 0; j < PK; j += 2) {
+    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(&sh.key[part * PK + j]);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) above[i] += (kk.x > kc[i]) + (kk.y > kc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) sh.rank[part][c0 + i * CS] = above[i];
   lds_barrier();
   if (tid < kWave) {
     const int lane = tid;
@@ -116,7 +125,7 @@ __device__ __forceinline__ void select_channels_block(const T* __restrict__ q, i
   ChannelQ<T, G> cq;
   cq.load(q, b, h, Hkv, D);
   select_channels_phase1<T, G>(cq, D, sh);
-  select_channels_phase2(D, r, sh);
+  select_channels_phase2<4, 256>(D, r, sh);
 }
 
 // Channel partition of the page-score sum: group g (of 16) sums chosen channels g, g+16, g+32,

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
     mg.missing = 0u;
   }
   select_channels_phase1<T, G>(cq, D, ch);
-  select_channels_phase2<kThreads / kApproxMaxD>(D, a.r, ch);
+  select_channels_phase2<8, kThreads>(D, a.r, ch);
   unsigned epoch = epoch_prev + 1u;
   if (epoch == 0u) epoch = 1u;  // tag 0 is what a cleared workspace holds
   const size_t sbase = (size_t)bh * D * a.s_pitch;
