@@ -181,7 +181,9 @@ int rkv_topk_select(const float* scores, int rows, int n, int k, int32_t* idx_ou
  * k_c, v_c  [B, Hkv, Lc, D]
  * page_idx  [B, Hkv, n_pages] int32 page numbers in [0, ceil(Lc/page_size)), each at most
  *           once (entries outside that range are ignored)
- * out       [B, Hq, D] out (dtype of the call; bf16 rounds to nearest even)
+ * out       [B, Hq, D] out (dtype of the call; bf16 rounds to nearest even). Scores, softmax
+ *           and sums are float32; for bf16 with D = 128 the product with V runs on matrix cores
+ *           with the softmax weights rounded to bf16.
  * Requires 1 <= n_pages <= ceil(Lc/page_size), n_pages <= 262144, D in {64, 128},
  * Hq / Hkv <= 8, scale finite.
  * ws        workspace of rkv_sparse_attend_workspace_bytes(...) bytes (may be 0, then NULL ok).
