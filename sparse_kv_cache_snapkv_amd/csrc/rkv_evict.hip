@@ -12,8 +12,9 @@
 //   gather  compressed K/V rows
 // bf16 logits use MFMA (v_mfma_f32_32x32x16_bf16): the window rows stay in LDS, every wave
 // streams 64 keys into registers and multiplies them against all row tiles. The dot product's
-// head-dim order is permuted identically in both operands (lane half h takes channels
-// h*D/2 + 8*s .. +8 at k-step s), so each lane reads one contiguous half row of K.
+// head dimension runs in the operands' natural order (lane half h takes channels 16s + 8h .. +8
+// at k-step s): the two lanes of a key then read 32 adjacent bytes per load, which streams K
+// faster than one contiguous half row per lane.
 // fp32 logits use plain FMAs (the small-workload path).
 #include <math.h>
 
@@ -85,8 +86,8 @@ EvictLayout layout_for(int B, int Hq, int Hkv, int L, int W, int keep, int dtype
 
 // ---------------------------------------------------------------------------- MFMA (bf16) passes
 
-// K rows of one wave's 64 keys (two 32-key tiles), in the permuted head-dim order of the MFMA
-// operands: lane (half hf, row n) holds channels hf*D/2 + 8s .. +8 of key key0 + kt*32 + n.
+// K rows of one wave's 64 keys (two 32-key tiles) as MFMA operands: at k-step s, lane (half hf,
+// row n) holds channels 16s + 8hf .. +8 of key key0 + kt*32 + n.
 template <int D>
 __device__ __forceinline__ void load_key_tiles(const bf16_t* __restrict__ k_bh, int key0,
                                                int last, int hf, int n,
@@ -94,9 +95,9 @@ __device__ __forceinline__ void load_key_tiles(const bf16_t* __restrict__ k_bh, 
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int key = min(key0 + kt * 32 + n, last);
-    const bf16_t* kr = k_bh + (size_t)key * D + hf * (D / 2);
+    const bf16_t* kr = k_bh + (size_t)key * D + hf * 8;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) kf[kt][s] = *reinterpret_cast<const bf16x8*>(kr + s * 8);
+    for (int s = 0; s < D / 16; ++s) kf[kt][s] = *reinterpret_cast<const bf16x8*>(kr + s * 16);
   }
 }
 
@@ -176,10 +177,10 @@ __global__ __launch_bounds__(kThreads) void k_win_stats_mfma(const bf16_t* __res
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[kt][i] = 0.f;
-      const uint16_t* qrow = smem + (size_t)(rt * 32 + n) * QS + hf * (D / 2);
+      const uint16_t* qrow = smem + (size_t)(rt * 32 + n) * QS + hf * 8;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrow + s * 8);
+        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
         acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][s], qf, acc[0], 0, 0, 0);
         acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][s], qf, acc[1], 0, 0, 0);
       }
@@ -296,10 +297,10 @@ __global__ __launch_bounds__(kThreads) void k_win_colsum_mfma(const bf16_t* __re
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[kt][i] = 0.f;
-      const uint16_t* qrow = smem + (size_t)(rt * 32 + n) * QS + hf * (D / 2);
+      const uint16_t* qrow = smem + (size_t)(rt * 32 + n) * QS + hf * 8;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrow + s * 8);
+        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
         acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[0][s], acc[0], 0, 0, 0);
         acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[1][s], acc[1], 0, 0, 0);
       }

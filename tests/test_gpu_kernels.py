@@ -301,6 +301,35 @@ def test_snapkvpp_evict_odd_key_groups_multiblock_topk(rkv):
     _evict_check(rkv, wf, gen.prompt_layer(wf))
 
 
+# (G, W, D): window rows G*W from one 32-row tile to 16 tiles; 120 rows end in a partial tile,
+# and above 256 rows the rows split into parts of unequal size (288 and 480 rows).
+ROW_TILE_CASES = [(1, 32, 128), (2, 32, 64), (3, 32, 128), (5, 24, 128), (5, 32, 64),
+                  (6, 32, 128), (7, 32, 128), (8, 32, 64), (9, 32, 128), (15, 32, 64),
+                  (16, 32, 128)]
+
+
+@pytest.mark.parametrize("G,W,D", ROW_TILE_CASES, ids=[f"g{g}-w{w}-d{d}" for g, w, d in ROW_TILE_CASES])
+def test_snapkvpp_evict_row_tiles(rkv, G, W, D):
+    w = configs.SMALL[1].replace(name=f"tiles-g{G}-w{W}-d{D}", B=1, Hq=2 * G, Hkv=2, D=D, L=2111,
+                                 W=W, keep=530, pool_kernel=15, n_needles=4, cfg_id=60 + G)
+    _evict_check(rkv, w, gen.prompt_layer(w))
+
+
+def test_snapkvpp_evict_logit_jump_in_a_later_key_group(rkv):
+    # 70000 keys over 2 KV heads: every pass-1 block takes two key groups. A key planted in the
+    # second group of its block scores about 90 nats above the rest for one window row, so that
+    # row's running maximum jumps there and the first group's sum is rescaled to almost nothing.
+    w = configs.SMALL[1].replace(name="jump", B=1, Hq=8, Hkv=2, D=128, L=70000, W=32, keep=9000,
+                                 pool_kernel=15, n_needles=4, cfg_id=70)
+    d = gen.prompt_layer(w)
+    nchunk = -(-((w.L + 255) // 256) // 2)  # chunks of two 256-key groups
+    pos = (1 * nchunk + 5) * 256 + 10       # group 1 of chunk 5
+    for h in range(w.Hkv):
+        q = O.widen(d["q_win"][0, h * w.G, 3]) * 8.0  # exact in bf16: a power-of-two multiple
+        d["k"][0, h, pos] = gen.to_storage(q.astype(np.float32), w.dtype)
+    _evict_check(rkv, w, d)
+
+
 def test_evict_indices_only(rkv):
     w = configs.TINY_FP32
     d = gen.prompt_layer(w)
