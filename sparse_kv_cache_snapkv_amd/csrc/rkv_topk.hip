@@ -57,20 +57,23 @@ __host__ __device__ constexpr int level_shift(int lev) { return lev == 0 ? 21 : 
 __host__ __device__ constexpr int level_bits(int lev) { return lev == 2 ? 10 : 11; }
 __host__ __device__ constexpr int level_bins(int lev) { return 1 << level_bits(lev); }
 
+// Per block of the last digit level: the suffix sums S[d] (its keys under the row's prefix with
+// a last digit >= d, d < 1024) and, in word 1024, its keys above the prefix.
+constexpr int kLastBins = level_bins(kLevels - 1);
+constexpr int kStateWords = kLastBins + 1;
+
 struct LongLayout {
   int nblk;
-  size_t off_hist, off_cnt, off_thr, total;
+  size_t off_hist, off_state, total;
 };
 
 LongLayout long_layout(int rows, int n) {
   LongLayout lo{};
   lo.nblk = (n + kLongChunk - 1) / kLongChunk;
   lo.off_hist = 0;
-  lo.off_cnt = lo.off_hist + (size_t)rows * kLevels * kHistStride * sizeof(uint32_t);
-  lo.off_cnt = (lo.off_cnt + 255) & ~(size_t)255;
-  lo.off_thr = lo.off_cnt + (size_t)rows * lo.nblk * 2 * sizeof(uint32_t);
-  lo.off_thr = (lo.off_thr + 255) & ~(size_t)255;
-  lo.total = lo.off_thr + (size_t)rows * 2 * sizeof(uint32_t);
+  lo.off_state = lo.off_hist + (size_t)rows * kLevels * kHistStride * sizeof(uint32_t);
+  lo.off_state = (lo.off_state + 255) & ~(size_t)255;
+  lo.total = lo.off_state + (size_t)rows * lo.nblk * kStateWords * sizeof(uint32_t);
   lo.total = (lo.total + 255) & ~(size_t)255;
   return lo;
 }
@@ -132,10 +135,15 @@ __device__ __forceinline__ void long_prefix(const uint32_t* __restrict__ hist_ro
   }
 }
 
+// The row's histogram of digit level LEVEL over the keys under the prefix the earlier levels
+// fixed. The last level also leaves each block's own counts (suffix sums of its digit histogram
+// and its keys above the prefix) in `state`, from which the write launch places every block's
+// keys without a counting pass of its own.
 template <int LEVEL>
 __global__ __launch_bounds__(kBlockThreads) void k_long_hist(const float* __restrict__ scores,
                                                             int n, int k,
-                                                            uint32_t* __restrict__ hist) {
+                                                            uint32_t* __restrict__ hist,
+                                                            uint32_t* __restrict__ state) {
   __shared__ SelectShared<kBlockThreads> sh;
   __shared__ uint32_t lh[kHistStride];
   const int tid = threadIdx.x, row = blockIdx.y;
@@ -154,68 +162,62 @@ __global__ __launch_bounds__(kBlockThreads) void k_long_hist(const float* __rest
     v[j] = 0.f;
     if (j * kBlockThreads + tid < nv) v[j] = s[j * kBlockThreads + tid];
   }
+  uint32_t above = 0;  // keys above the prefix (counted on the last level only)
 #pragma unroll
   for (int j = 0; j < kLongPer; ++j) {
     const uint32_t key = order_key(v[j]);
-    const bool match = j * kBlockThreads + tid < nv &&
-                       (top >= 32 || (key >> top) == (prefix >> top));
+    const bool valid = j * kBlockThreads + tid < nv;
+    const bool match = valid && (top >= 32 || (key >> top) == (prefix >> top));
     if (match) atomicAdd(&lh[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+    if constexpr (LEVEL == kLevels - 1) above += (valid && (key >> top) > (prefix >> top)) ? 1u : 0u;
   }
   __syncthreads();
   uint32_t* hl = hist_row + LEVEL * kHistStride;
   for (int i = tid; i < nbins; i += kBlockThreads)
     if (lh[i] != 0u) atomicAdd(&hl[i], lh[i]);
-}
-
-// Threshold key T and the number of keys equal to T to take; per-block counts of the keys above
-// and equal to T. Block 0 of each row also stores (T, need) for the write launch.
-__global__ __launch_bounds__(kBlockThreads) void k_long_count(const float* __restrict__ scores,
-                                                             int n, int k,
-                                                             const uint32_t* __restrict__ hist,
-                                                             uint32_t* __restrict__ cnt,
-                                                             uint32_t* __restrict__ thr) {
-  __shared__ SelectShared<kBlockThreads> sh;
-  const int tid = threadIdx.x, row = blockIdx.y, nblk = gridDim.x;
-  uint32_t T, need;
-  long_prefix(hist + (size_t)row * kLevels * kHistStride, kLevels, (uint32_t)k, T, need, sh);
-  const float* s = scores + (size_t)row * n + (size_t)blockIdx.x * kLongChunk;
-  const int nv = min(kLongChunk, n - (int)blockIdx.x * kLongChunk);
-  uint32_t gt = 0, eq = 0;
+  if constexpr (LEVEL == kLevels - 1) {
+    // thread t holds digits nbins-1-4t down to nbins-4-4t; the exclusive scan over the threads
+    // gives the keys in the digits above them
+    constexpr int bpt = nbins / kBlockThreads;
+    uint32_t c[bpt], local = 0;
 #pragma unroll
-  for (int j = 0; j < kLongPer; ++j) {
-    const int i = j * kBlockThreads + tid;
-    float x = 0.f;
-    if (i < nv) x = s[i];
-    const uint32_t key = order_key(x);
-    gt += (i < nv && key > T) ? 1u : 0u;
-    eq += (i < nv && key == T) ? 1u : 0u;
-  }
-  uint32_t e0, e1, tg, te;
-  block_scan2<kBlockThreads>(gt, eq, e0, e1, tg, te, sh, 1);
-  if (tid == 0) {
-    cnt[((size_t)row * nblk + blockIdx.x) * 2] = tg;
-    cnt[((size_t)row * nblk + blockIdx.x) * 2 + 1] = te;
-    if (blockIdx.x == 0) {
-      thr[(size_t)row * 2] = T;
-      thr[(size_t)row * 2 + 1] = need;
+    for (int j = 0; j < bpt; ++j) {
+      c[j] = lh[nbins - 1 - (tid * bpt + j)];
+      local += c[j];
     }
+    uint32_t excl, unused, tot, above_tot;
+    block_scan2<kBlockThreads>(local, above, excl, unused, tot, above_tot, sh, 1);
+    uint32_t* st = state + ((size_t)row * gridDim.x + blockIdx.x) * kStateWords;
+    uint32_t run = excl;
+#pragma unroll
+    for (int j = 0; j < bpt; ++j) {
+      run += c[j];
+      st[nbins - 1 - (tid * bpt + j)] = run;
+    }
+    if (tid == 0) st[kLastBins] = above_tot;
   }
 }
 
+// Threshold key T (from the three histograms) and the number of keys equal to T to take; the
+// keys above and equal to T in the blocks before this one come from their last-level counts;
+// then the block writes its selected positions in order.
 __global__ __launch_bounds__(kBlockThreads) void k_long_write(const float* __restrict__ scores,
                                                              int n, int k,
-                                                             const uint32_t* __restrict__ cnt,
-                                                             const uint32_t* __restrict__ thr,
+                                                             const uint32_t* __restrict__ hist,
+                                                             const uint32_t* __restrict__ state,
                                                              int32_t* __restrict__ out,
                                                              int out_stride) {
   __shared__ SelectShared<kBlockThreads> sh;
   const int tid = threadIdx.x, row = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
-  const uint32_t T = thr[(size_t)row * 2], need = thr[(size_t)row * 2 + 1];
-  // keys above / equal to T in the blocks before this one
+  uint32_t T, need;
+  long_prefix(hist + (size_t)row * kLevels * kHistStride, kLevels, (uint32_t)k, T, need, sh);
+  const uint32_t d = T & (uint32_t)(kLastBins - 1);  // T's last digit
   uint32_t bgt = 0, beq = 0;
   for (int b = tid; b < blk; b += kBlockThreads) {
-    bgt += cnt[((size_t)row * nblk + b) * 2];
-    beq += cnt[((size_t)row * nblk + b) * 2 + 1];
+    const uint32_t* st = state + ((size_t)row * nblk + b) * kStateWords;
+    const uint32_t sd = st[d], sd1 = d + 1 < (uint32_t)kLastBins ? st[d + 1] : 0u;
+    bgt += st[kLastBins] + sd1;
+    beq += sd - sd1;
   }
   uint32_t e0, e1, gt_base, eq_base;
   block_scan2<kBlockThreads>(bgt, beq, e0, e1, gt_base, eq_base, sh, 0);
@@ -257,8 +259,7 @@ hipError_t long_launches(const float* scores, int rows, int n, int k, int32_t* o
   const LongLayout lo = long_layout(rows, n);
   char* w = static_cast<char*>(ws);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + lo.off_hist);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + lo.off_cnt);
-  uint32_t* thr = reinterpret_cast<uint32_t*>(w + lo.off_thr);
+  uint32_t* state = reinterpret_cast<uint32_t*>(w + lo.off_state);
   const dim3 lgrid(lo.nblk, rows);
   hipError_t e;
   if (!cleared) {
@@ -267,17 +268,17 @@ hipError_t long_launches(const float* scores, int rows, int n, int k, int32_t* o
                        dim3(256), 0, stream, hist, nhist);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_long_hist<0>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  hipLaunchKernelGGL(k_long_hist<0>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist,
+                     state);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_hist<1>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  hipLaunchKernelGGL(k_long_hist<1>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist,
+                     state);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_hist<2>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist);
+  hipLaunchKernelGGL(k_long_hist<2>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist,
+                     state);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_count, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist, cnt,
-                     thr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_long_write, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, cnt, thr,
-                     out, out_stride);
+  hipLaunchKernelGGL(k_long_write, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist,
+                     state, out, out_stride);
   return hipGetLastError();
 }
 
