@@ -513,8 +513,8 @@ __global__ __launch_bounds__(kThreads) void k_gather(const T* __restrict__ k,
   if (k_out == nullptr) return;
   const size_t si = ((size_t)bh * L + src) * D + li * V;
   const size_t di = ((size_t)bh * Lc + t) * D + li * V;
-  *reinterpret_cast<uint4*>(k_out + di) = load16(k + si);
-  *reinterpret_cast<uint4*>(v_out + di) = load16(v + si);
+  store16_stream(k_out + di, load16(k + si));
+  store16_stream(v_out + di, load16(v + si));
 }
 
 template <typename T, int D>

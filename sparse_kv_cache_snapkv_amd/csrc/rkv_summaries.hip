@@ -99,8 +99,8 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
         for (int s = 0; s < kSlots; ++s) {
           if (base + s >= nt[i]) continue;
           const int t = t0[i] + base + s;
-          *reinterpret_cast<uint4*>(ko + (size_t)t * D + ch * V) = raw[i][s];
-          *reinterpret_cast<uint4*>(vo + (size_t)t * D + ch * V) = rawv[i][s];
+          store16_stream(ko + (size_t)t * D + ch * V, raw[i][s]);
+          store16_stream(vo + (size_t)t * D + ch * V, rawv[i][s]);
           if (ch == 0 && (g.identity || t >= nsel)) g.kept[(size_t)bh * Lc + t] = src[i][s];
         }
       }
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
       uint4 wmn, wmx;
       __builtin_memcpy(&wmn, vmn, 16);
       __builtin_memcpy(&wmx, vmx, 16);
-      *reinterpret_cast<uint4*>(dmn) = wmn;
-      *reinterpret_cast<uint4*>(dmx) = wmx;
+      store16_stream(dmn, wmn);
+      store16_stream(dmx, wmx);
     } else {
       for (int e = 0; e < kVecP && pv + e < np; ++e) {
         dmn[e] = from_f32<T>(smin[c][pv + e]);
