@@ -14,9 +14,8 @@ GPU before timing; each stage is captured once as a HIP graph and replayed, all 
 
 value = mean fused decode-step latency (us) over the timed steps and top-k budgets; the JSON line
 also carries per-top-k latency and GB/s, the dominant kernel's roofline, and, outside the timed
-region: the per-stage split (the same steps as three separate calls), the eviction with the page
-summaries in one pass (stages.evict_summarized), the multi-turn step over the full 131072-token
-caches, a growing cache, selection quality, the other workloads (2K fp32,
+region: the per-stage split (the same steps as three separate calls), the multi-turn step over
+the full 131072-token caches, a growing cache, selection quality, the other workloads (2K fp32,
 32K, batch 16 at 32K, the 80-layer 70B-shaped stack at 256K, one 70B-shaped layer's eviction)
 and the CPU oracle's time on bounded samples of every workload.
 """
@@ -651,37 +650,6 @@ def extra(rkv, torch, gen, w, line, prompts, kept, k_c, v_c, kmin, kmax, q_dec, 
                                  append_plus_step_us=round(grow["append+step"], 3),
                                  step_topk=tk_g, sync_status=rkv.decode_workspace_status(ws_g))
     del kc_g, vc_g, kmin_g, kmax_g, ws_g
-
-    progress("eviction with the page summaries in one pass")
-    # SnapKV++'s compaction writing the page summaries as it copies the kept rows (one pass over
-    # them instead of a gather and a summary pass over its output), per layer replica, into one
-    # replica's worth of separate buffers; its results must equal the separate calls' bit for bit
-    kept_f, kc_f, vc_f = torch.empty_like(kept[0]), torch.empty_like(k_c[0]), torch.empty_like(v_c[0])
-    kmin_f, kmax_f = torch.empty_like(kmin[0]), torch.empty_like(kmax[0])
-    dcode = 1 if dt == torch.bfloat16 else 0
-    ws_f = torch.empty(max(1, rkv.snapkvpp_workspace_bytes(B, Hq, Hkv, w.L, D, w.W, w.keep, dcode)),
-                       dtype=torch.uint8, device=dev)
-
-    def fused_all():
-        for r in range(R):
-            p = prompts[r]
-            rkv.rkv_snapkvpp_evict_summarized(p["q_win"], p["k"], p["v"], w.keep, w.pool_kernel,
-                                              w.page_size, "avg", scale, kept_idx=kept_f,
-                                              k_out=kc_f, v_out=vc_f, kmin_t=kmin_f,
-                                              kmax_t=kmax_f, workspace=ws_f)
-
-    us = replay_us(torch, capture(torch, fused_all), reps) / R
-    torch.cuda.synchronize()
-    same = bool(torch.equal(kept_f, kept[R - 1])) and all(
-        torch.equal(a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16
-        else torch.equal(a, b)
-        for a, b in ((kc_f, k_c[R - 1]), (vc_f, v_c[R - 1]), (kmin_f, kmin[R - 1]),
-                     (kmax_f, kmax[R - 1])))
-    ab = algorithmic_bytes(w, w.topk[0])
-    nb = ab["evict"] + ab["summaries"] - B * Hkv * w.Lc * D * w.elem_bytes  # no re-read of K_c
-    line["stages"]["evict_summarized"] = dict(us_per_layer=round(us, 2), algorithmic_bytes=nb,
-                                              GBps=gbps(nb, us), equal_to_separate_calls=same)
-    del kept_f, kc_f, vc_f, kmin_f, kmax_f, ws_f
 
     progress("selection quality")
     # selection quality against Exact-TopK (replica 0, the first decode steps): RocketKV's split

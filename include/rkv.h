@@ -119,21 +119,6 @@ int rkv_snapkvpp_evict(const void* q_win, const void* k, const void* v, int B, i
                        int dtype, int32_t* kept_idx, void* k_out, void* v_out, float* pooled_out,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* rkv_snapkvpp_evict followed by rkv_build_page_summaries(k_out, ..., page_size, ...) of the
- * compressed keys, with the same results bit for bit, in one pass over the kept rows: the
- * compaction writes each page's minimum and maximum as it copies the page's keys (the page
- * summaries of [rebuttal] "Explanation of Calculating Approximate Attention Scores", built from
- * the cache SnapKV++ keeps).
- * kmin_t, kmax_t [B, Hkv, D, ceil(Lc / page_size)]  out, channel-major, as rkv_build_page_summaries
- * k_out, v_out, kmin_t and kmax_t are required (RKV_ERR_NULL otherwise); page_size >= 1. The
- * other arguments, the workspace and the errors are those of rkv_snapkvpp_evict. */
-int rkv_snapkvpp_evict_summarized(const void* q_win, const void* k, const void* v, int B, int Hq,
-                                  int Hkv, int L, int D, int W, int keep, int pool_kernel,
-                                  int pool_type, float scale, int dtype, int page_size,
-                                  int32_t* kept_idx, void* k_out, void* v_out, void* kmin_t,
-                                  void* kmax_t, float* pooled_out, void* ws, size_t ws_bytes,
-                                  void* stream);
-
 /* ------------------------------------------------------------------------------------------
  * Page summaries ([rebuttal] "Explanation of Calculating Approximate Attention Scores", paper
  * Figure 3: K is split into pages of consecutive tokens and each page keeps its element-wise

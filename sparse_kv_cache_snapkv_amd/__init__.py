@@ -21,7 +21,6 @@ from .api import (  # noqa: F401
     rkv_plan_budget,
     rkv_hybrid_approx_scores,
     rkv_snapkvpp_evict,
-    rkv_snapkvpp_evict_summarized,
     rkv_sparse_attend_decode,
     rkv_topk_select,
     snapkvpp_workspace_bytes,

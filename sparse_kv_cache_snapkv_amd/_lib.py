@@ -18,8 +18,6 @@ SIGNATURES = {
     "rkv_snapkvpp_workspace_bytes": (_c_int, [_c_int] * 8 + [_szp]),
     "rkv_snapkvpp_evict": (_c_int, [_vp, _vp, _vp] + [_c_int] * 9 + [_c_float, _c_int]
                            + [_vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
-    "rkv_snapkvpp_evict_summarized": (_c_int, [_vp, _vp, _vp] + [_c_int] * 9 + [_c_float]
-                                      + [_c_int] * 2 + [_vp] * 7 + [_c_size, _vp]),
     "rkv_build_page_summaries": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp]),
     "rkv_hybrid_approx_scores": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp, _vp, _vp]),
     "rkv_topk_workspace_bytes": (_c_int, [_c_int] * 3 + [_szp]),

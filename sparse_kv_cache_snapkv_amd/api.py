@@ -128,55 +128,6 @@ def rkv_snapkvpp_evict(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ke
     return kept_idx, k_out, v_out
 
 
-def rkv_snapkvpp_evict_summarized(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                                  keep: int, pool_kernel: int, page_size: int,
-                                  pool_type: str = "avg", scale: Optional[float] = None, *,
-                                  kept_idx: Optional[torch.Tensor] = None,
-                                  k_out: Optional[torch.Tensor] = None,
-                                  v_out: Optional[torch.Tensor] = None,
-                                  kmin_t: Optional[torch.Tensor] = None,
-                                  kmax_t: Optional[torch.Tensor] = None,
-                                  pooled_out: Optional[torch.Tensor] = None,
-                                  workspace: Optional[torch.Tensor] = None):
-    """SnapKV++ eviction with the page summaries of the compressed keys in the same pass.
-    -> (kept_idx, k_c, v_c, kmin_t, kmax_t), as rkv_snapkvpp_evict then rkv_build_page_summaries."""
-    B, Hq, W, D = q_win.shape
-    Hkv, L = k.shape[1], k.shape[2]
-    dt = _dtype_code(k)
-    Lc = min(keep, L)
-    P = -(-Lc // page_size)
-    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _shape(k, "k", (B, Hkv, L, D))
-    _shape(v, "v", (B, Hkv, L, D))
-    _shape(kept_idx, "kept_idx", (B, Hkv, Lc))
-    _shape(k_out, "k_out", (B, Hkv, Lc, D))
-    _shape(v_out, "v_out", (B, Hkv, Lc, D))
-    _shape(kmin_t, "kmin_t", (B, Hkv, D, P))
-    _shape(kmax_t, "kmax_t", (B, Hkv, D, P))
-    _shape(pooled_out, "pooled_out", (B, Hkv, max(L - W, 1)))
-    if kept_idx is None:
-        kept_idx = torch.empty((B, Hkv, Lc), dtype=torch.int32, device=k.device)
-    if k_out is None:
-        k_out = torch.empty((B, Hkv, Lc, D), dtype=k.dtype, device=k.device)
-    if v_out is None:
-        v_out = torch.empty((B, Hkv, Lc, D), dtype=k.dtype, device=k.device)
-    if kmin_t is None:
-        kmin_t = torch.empty((B, Hkv, D, P), dtype=k.dtype, device=k.device)
-    if kmax_t is None:
-        kmax_t = torch.empty((B, Hkv, D, P), dtype=k.dtype, device=k.device)
-    nbytes = snapkvpp_workspace_bytes(B, Hq, Hkv, L, D, W, keep, dt)
-    ws, wsb = _workspace(k, nbytes, workspace)
-    _check("rkv_snapkvpp_evict_summarized", _lib.load().rkv_snapkvpp_evict_summarized(
-        _dev(q_win, "q_win", k.dtype), _dev(k, "k"), _dev(v, "v", k.dtype), B, Hq, Hkv, L, D, W,
-        keep, pool_kernel, POOL[pool_type], scale, dt, page_size,
-        _dev(kept_idx, "kept_idx", torch.int32), _dev(k_out, "k_out", k.dtype),
-        _dev(v_out, "v_out", k.dtype), _dev(kmin_t, "kmin_t", k.dtype),
-        _dev(kmax_t, "kmax_t", k.dtype),
-        _dev(pooled_out, "pooled_out", torch.float32) if pooled_out is not None else None,
-        ws, wsb, _stream(k)))
-    return kept_idx, k_out, v_out, kmin_t, kmax_t
-
-
 def rkv_build_page_summaries(k_c: torch.Tensor, page_size: int, *,
                              kmin_t: Optional[torch.Tensor] = None,
                              kmax_t: Optional[torch.Tensor] = None):

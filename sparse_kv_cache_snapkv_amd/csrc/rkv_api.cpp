@@ -133,27 +133,8 @@ int rkv_snapkvpp_evict(const void* q_win, const void* k, const void* v, int B, i
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return RKV_ERR_WORKSPACE;
   return launch_status(rkv::launch_evict(q_win, k, v, B, Hq, Hkv, L, D, W, keep, pool_kernel,
                                          pool_type, scale, dtype, kept_idx, k_out, v_out,
-                                         keep >= L ? nullptr : pooled_out, ws, 0, nullptr, nullptr,
+                                         keep >= L ? nullptr : pooled_out, ws,
                                          static_cast<hipStream_t>(stream)));
-}
-
-int rkv_snapkvpp_evict_summarized(const void* q_win, const void* k, const void* v, int B, int Hq,
-                                  int Hkv, int L, int D, int W, int keep, int pool_kernel,
-                                  int pool_type, float scale, int dtype, int page_size,
-                                  int32_t* kept_idx, void* k_out, void* v_out, void* kmin_t,
-                                  void* kmax_t, float* pooled_out, void* ws, size_t ws_bytes,
-                                  void* stream) {
-  if (!k_out || !v_out || !kmin_t || !kmax_t) return RKV_ERR_NULL;
-  int st = check_evict(q_win, k, v, B, Hq, Hkv, L, D, W, keep, pool_kernel, pool_type, scale,
-                       dtype, kept_idx, k_out, v_out);
-  if (st != RKV_OK) return st;
-  if (page_size < 1) return RKV_ERR_SHAPE;
-  const size_t need = rkv::evict_ws_bytes(B, Hq, Hkv, L, D, W, keep, dtype);
-  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return RKV_ERR_WORKSPACE;
-  return launch_status(rkv::launch_evict(q_win, k, v, B, Hq, Hkv, L, D, W, keep, pool_kernel,
-                                         pool_type, scale, dtype, kept_idx, k_out, v_out,
-                                         keep >= L ? nullptr : pooled_out, ws, page_size, kmin_t,
-                                         kmax_t, static_cast<hipStream_t>(stream)));
 }
 
 int rkv_build_page_summaries(const void* k_c, int B, int Hkv, int Lc, int D, int page_size,

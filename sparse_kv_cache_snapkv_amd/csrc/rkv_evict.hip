@@ -614,16 +614,10 @@ size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int
 hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, int Hq, int Hkv,
                         int L, int D, int W, int keep, int pool_kernel, int pool_type, float scale,
                         int dtype, int32_t* kept_idx, void* k_out, void* v_out, float* pooled_out,
-                        void* ws, int page_size, void* kmin_t, void* kmax_t, hipStream_t stream) {
+                        void* ws, hipStream_t stream) {
   const int BH = B * Hkv;
-  // the compaction, alone or with the page summaries of the compacted keys
-  auto compact = [&](int Lc, int identity) {
-    if (kmin_t != nullptr)
-      return launch_gather_summaries(k, v, BH, L, W, Lc, identity, kept_idx, k_out, v_out, D,
-                                     page_size, dtype, kmin_t, kmax_t, stream);
-    return gather_any(dtype, D, k, v, BH, L, W, Lc, identity, kept_idx, k_out, v_out, stream);
-  };
-  if (keep >= L) return compact(L, 1);
+  if (keep >= L)
+    return gather_any(dtype, D, k, v, BH, L, W, L, 1, kept_idx, k_out, v_out, stream);
   const EvictLayout lo = layout_for(B, Hq, Hkv, L, W, keep, dtype);
   char* w = static_cast<char*>(ws);
   const float scale2 = scale * kLog2e;
@@ -654,7 +648,7 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
                                     stream)
               : launch_topk(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk, stream);
   if (e != hipSuccess) return e;
-  return compact(keep, 0);
+  return gather_any(dtype, D, k, v, BH, L, W, keep, 0, kept_idx, k_out, v_out, stream);
 }
 
 }  // namespace rkv

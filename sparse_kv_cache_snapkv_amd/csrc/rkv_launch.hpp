@@ -16,13 +16,6 @@ int device_cus();
 hipError_t launch_page_minmax(const void* k_c, const int32_t* rows, int BH, int Lc, int kv_pitch,
                               int cap, int D, int page_size, int dtype, void* kmin_t,
                               void* kmax_t, hipStream_t stream);
-// SnapKV++'s compaction (slot t of the Lc = min(keep, L) outputs from the kept prefix position or
-// the window, or t itself with identity) with the page summaries of the compacted keys, in one
-// pass over the kept rows: the same bits as the compaction followed by launch_page_minmax.
-hipError_t launch_gather_summaries(const void* k, const void* v, int BH, int L, int W, int Lc,
-                                   int identity, int32_t* kept, void* k_out, void* v_out, int D,
-                                   int page_size, int dtype, void* kmin_t, void* kmax_t,
-                                   hipStream_t stream);
 
 // One token per (b, h) into slot Lc of caches of capacity cap, folded into its page summary.
 hipError_t launch_kv_append(const void* k_new, const void* v_new, int BH, int Lc, int cap, int D,
@@ -100,11 +93,9 @@ hipError_t launch_decode_step_noalloc(const void* q, const void* kmin_t, const v
 
 // SnapKV++ eviction.
 size_t evict_ws_bytes(int B, int Hq, int Hkv, int L, int D, int W, int keep, int dtype);
-// With kmin_t (then k_out, v_out and kmax_t too), the compaction also writes the page summaries
-// of the compacted keys (page_size slots per page), through launch_gather_summaries.
 hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, int Hq, int Hkv,
                         int L, int D, int W, int keep, int pool_kernel, int pool_type, float scale,
                         int dtype, int32_t* kept_idx, void* k_out, void* v_out, float* pooled_out,
-                        void* ws, int page_size, void* kmin_t, void* kmax_t, hipStream_t stream);
+                        void* ws, hipStream_t stream);
 
 }  // namespace rkv

@@ -2,9 +2,7 @@
 // channel-major so a decode step reads each selected channel's page row contiguously.
 // (RocketKV rebuttal, "Explanation of Calculating Approximate Attention Scores", Figure 3.)
 // Also the decode-time append of one token per (b, h), which folds the new K row into the
-// summary of its page (the tail page grows; a token at a page boundary starts a new page), and
-// SnapKV++'s compaction folded into the summaries of the compacted keys (one pass over the kept
-// rows instead of a gather followed by a pass over its output).
+// summary of its page (the tail page grows; a token at a page boundary starts a new page).
 #include "rkv_common.hpp"
 #include "rkv_launch.hpp"
 
@@ -15,34 +13,19 @@ namespace {
 constexpr int kPagesPerBlock = 32;
 constexpr int kThreads = 256;
 
-// The compaction a summary launch may perform on the way (GATHER): slot t of head bh comes from
-// row src(t) of the full caches (L rows per head), src(t) = t when nothing is evicted, else the
-// kept prefix position kept[bh*Lc + t] (clamped into [0, L - W)) for t < Lc - W and window row
-// L - W + (t - (Lc - W)) after. K and V of that row go to slot t of k_out / v_out, and the window
-// (or identity) slots' positions are written into kept.
-struct GatherArgs {
-  const void* v;
-  void* k_out;
-  void* v_out;
-  int32_t* kept;
-  int L, W, identity;
-};
-
 // One block: kPagesPerBlock pages of one (b, h). Reads token rows as 16-byte chunks, reduces
 // over each page's slots, transposes through LDS and writes [D][pages] rows. The cache holds
 // kv_pitch token slots per head (the first Lc valid) and a summary row s_pitch pages. rows (may
 // be null): slot t of head bh is row rows[bh*Lc + t] of the cache, clamped into [0, kv_pitch).
-// GATHER: slot t's row is the compaction's src(t) instead (kv_pitch = L), and its K and V chunks
-// are also written to the compacted caches. A thread owns kItems (page, chunk) items; the loads of
-// kSlots slots of all of them are issued before any is folded (the slots of a page fold in slot
-// order, keeping the first of equal values, as the append does).
-template <typename T, int D, bool GATHER>
+// A thread owns kItems (page, chunk) items; the loads of kSlots slots of all of them are issued
+// before any is folded (the slots of a page fold in slot order, keeping the first of equal
+// values, as the append does).
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ k_c,
                                                           const int32_t* __restrict__ rows,
                                                           T* __restrict__ kmin_t,
                                                           T* __restrict__ kmax_t, int Lc, int P,
-                                                          int ps, int kv_pitch, int s_pitch,
-                                                          GatherArgs g) {
+                                                          int ps, int kv_pitch, int s_pitch) {
   constexpr int V = vec16<T>::n;
   constexpr int CH = D / V;  // 16-byte chunks per token row
   constexpr int kItems = kPagesPerBlock * CH / kThreads;
@@ -54,13 +37,6 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
   const int p0 = blockIdx.x * kPagesPerBlock;
   const T* kb = k_c + (size_t)bh * kv_pitch * D;
   const int32_t* rb = rows != nullptr ? rows + (size_t)bh * Lc : nullptr;
-  const T* vb = GATHER ? static_cast<const T*>(g.v) + (size_t)bh * kv_pitch * D : nullptr;
-  const int nsel = Lc - g.W;
-  auto src_of = [&](int t) -> int {
-    if (g.identity) return t;
-    if (t >= nsel) return g.L - g.W + (t - nsel);
-    return min(max(g.kept[(size_t)bh * Lc + t], 0), g.L - g.W - 1);
-  };
   int t0[kItems], nt[kItems];
   float mn[kItems][V], mx[kItems][V];
 #pragma unroll
@@ -71,37 +47,16 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
   }
   for (int base = 0; base < ps; base += kSlots) {
     uint4 raw[kItems][kSlots];
-    uint4 rawv[GATHER ? kItems : 1][kSlots];
-    int src[kItems][kSlots];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int ch = (i * kThreads + threadIdx.x) % CH;
 #pragma unroll
       for (int s = 0; s < kSlots; ++s) {
         raw[i][s] = make_uint4(0, 0, 0, 0);
-        src[i][s] = 0;
         if (base + s < nt[i]) {
           const int t = t0[i] + base + s;
-          const int r = GATHER ? src_of(t) : rb != nullptr ? min(max(rb[t], 0), kv_pitch - 1) : t;
-          src[i][s] = r;
+          const int r = rb != nullptr ? min(max(rb[t], 0), kv_pitch - 1) : t;
           raw[i][s] = load16(kb + (size_t)r * D + ch * V);
-          if constexpr (GATHER) rawv[i][s] = load16(vb + (size_t)r * D + ch * V);
-        }
-      }
-    }
-    if constexpr (GATHER) {
-      T* ko = static_cast<T*>(g.k_out) + (size_t)bh * Lc * D;
-      T* vo = static_cast<T*>(g.v_out) + (size_t)bh * Lc * D;
-#pragma unroll
-      for (int i = 0; i < kItems; ++i) {
-        const int ch = (i * kThreads + threadIdx.x) % CH;
-#pragma unroll
-        for (int s = 0; s < kSlots; ++s) {
-          if (base + s >= nt[i]) continue;
-          const int t = t0[i] + base + s;
-          store16_stream(ko + (size_t)t * D + ch * V, raw[i][s]);
-          store16_stream(vo + (size_t)t * D + ch * V, rawv[i][s]);
-          if (ch == 0 && (g.identity || t >= nsel)) g.kept[(size_t)bh * Lc + t] = src[i][s];
         }
       }
     }
@@ -198,21 +153,9 @@ hipError_t launch_t(const void* k_c, const int32_t* rows, int BH, int Lc, int kv
                     int ps, void* kmin_t, void* kmax_t, hipStream_t stream) {
   const int P = (Lc + ps - 1) / ps;
   dim3 grid((P + kPagesPerBlock - 1) / kPagesPerBlock, BH);
-  hipLaunchKernelGGL((k_page_minmax<T, D, false>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((k_page_minmax<T, D>), grid, dim3(kThreads), 0, stream,
                      static_cast<const T*>(k_c), rows, static_cast<T*>(kmin_t),
-                     static_cast<T*>(kmax_t), Lc, P, ps, kv_pitch, (cap + ps - 1) / ps,
-                     GatherArgs{nullptr, nullptr, nullptr, nullptr, 0, 0, 1});
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-hipError_t gather_t(const void* k, const GatherArgs& g, int BH, int Lc, int ps, void* kmin_t,
-                    void* kmax_t, hipStream_t stream) {
-  const int P = (Lc + ps - 1) / ps;
-  dim3 grid((P + kPagesPerBlock - 1) / kPagesPerBlock, BH);
-  hipLaunchKernelGGL((k_page_minmax<T, D, true>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const T*>(k), nullptr, static_cast<T*>(kmin_t),
-                     static_cast<T*>(kmax_t), Lc, P, ps, g.L, P, g);
+                     static_cast<T*>(kmax_t), Lc, P, ps, kv_pitch, (cap + ps - 1) / ps);
   return hipGetLastError();
 }
 
@@ -240,18 +183,6 @@ hipError_t launch_page_minmax(const void* k_c, const int32_t* rows, int BH, int 
                                         kmax_t, stream)
                  : launch_t<bf16_t, 128>(k_c, rows, BH, Lc, kv_pitch, cap, page_size, kmin_t,
                                          kmax_t, stream);
-}
-
-hipError_t launch_gather_summaries(const void* k, const void* v, int BH, int L, int W, int Lc,
-                                   int identity, int32_t* kept, void* k_out, void* v_out, int D,
-                                   int page_size, int dtype, void* kmin_t, void* kmax_t,
-                                   hipStream_t stream) {
-  const GatherArgs g{v, k_out, v_out, kept, L, W, identity};
-  if (dtype == 0)
-    return D == 64 ? gather_t<float, 64>(k, g, BH, Lc, page_size, kmin_t, kmax_t, stream)
-                   : gather_t<float, 128>(k, g, BH, Lc, page_size, kmin_t, kmax_t, stream);
-  return D == 64 ? gather_t<bf16_t, 64>(k, g, BH, Lc, page_size, kmin_t, kmax_t, stream)
-                 : gather_t<bf16_t, 128>(k, g, BH, Lc, page_size, kmin_t, kmax_t, stream);
 }
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, int BH, int Lc, int cap, int D,

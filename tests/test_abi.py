@@ -129,28 +129,6 @@ def test_evict_rejects_bad_arguments(lib):
     assert call(wsb=16) == -4
 
 
-
-def test_evict_summarized_rejects_bad_arguments(lib):
-    ev = lib.rkv_snapkvpp_evict_summarized
-    ok = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=4, Hkv=2, L=2048, D=64, W=16, keep=512, p=7, pt=0,
-              scale=0.125, dt=0, ps=4, kept=FAKE, ko=FAKE, vo=FAKE, kmin=FAKE, kmax=FAKE,
-              pooled=None, ws=FAKE, wsb=1 << 30, stream=None)
-
-    def call(**kw):
-        a = dict(ok, **kw)
-        return ev(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["W"],
-                  a["keep"], a["p"], a["pt"], a["scale"], a["dt"], a["ps"], a["kept"], a["ko"],
-                  a["vo"], a["kmin"], a["kmax"], a["pooled"], a["ws"], a["wsb"], a["stream"])
-
-    assert call(ko=None, vo=None) == -1             # the compressed cache is required here
-    assert call(kmin=None) == -1
-    assert call(kmax=None) == -1
-    assert call(kept=None) == -1
-    assert call(ps=0) == -2
-    assert call(keep=8) == -2
-    assert call(D=96) == -5
-    assert call(ws=None) == -4
-
 def test_decode_calls_reject_bad_arguments(lib):
     att = lib.rkv_sparse_attend_decode
     base = [FAKE, FAKE, FAKE, FAKE, 1, 32, 8, 16384, 128, 4, 32, 0.088, 1, FAKE, None, 0, None]

@@ -330,42 +330,6 @@ def test_snapkvpp_evict_logit_jump_in_a_later_key_group(rkv):
     _evict_check(rkv, w, d)
 
 
-# (workload, page_size, keep): bf16 and fp32, ragged pages, the multi-block kept-set top-k, and
-# nothing evicted
-SUMMARIZED_CASES = [(configs.SMALL[1], 4, None), (configs.SMALL[2], 3, None),
-                    (configs.SMALL[1].replace(name="summ-long", B=1, Hq=8, Hkv=2, L=12500,
-                                              keep=12000, cfg_id=33), 4, None),
-                    (configs.SMALL[3], 8, None), (configs.SMALL[1], 5, 4000)]
-
-
-@pytest.mark.parametrize("w,ps,keep", SUMMARIZED_CASES,
-                         ids=[f"{c[0].name}-ps{c[1]}-{c[2]}" for c in SUMMARIZED_CASES])
-def test_evict_summarized_equals_evict_then_summaries(rkv, w, ps, keep):
-    keep = w.keep if keep is None else keep
-    d = gen.prompt_layer(w)
-    q, k, v = T(d["q_win"]), T(d["k"]), T(d["v"])
-    kept, kc, vc = rkv.rkv_snapkvpp_evict(q, k, v, keep, w.pool_kernel)
-    kmin, kmax = rkv.rkv_build_page_summaries(kc, ps)
-    kept2, kc2, vc2, kmin2, kmax2 = rkv.rkv_snapkvpp_evict_summarized(q, k, v, keep, w.pool_kernel,
-                                                                      ps)
-    torch.cuda.synchronize()
-    assert torch.equal(kept, kept2)
-    for a, b in ((kc, kc2), (vc, vc2), (kmin, kmin2), (kmax, kmax2)):
-        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
-                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
-    # and against the oracle's summaries of the oracle's compressed keys
-    ref = O.snapkvpp_evict(d["q_win"], d["k"], d["v"], keep, w.pool_kernel, 1 / math.sqrt(w.D))
-    kp = kept2.cpu().numpy()
-    k64 = O.widen(d["k"])
-    for b in range(w.B):
-        for h in range(w.Hkv):
-            rows = k64[b, h, kp[b, h].astype(np.int64)]
-            mn, mx = O.page_summaries(rows, ps)
-            assert np.array_equal(O.widen(H(kmin2[b, h])), mn)
-            assert np.array_equal(O.widen(H(kmax2[b, h])), mx)
-    assert ref["kept"].shape == kp.shape
-
-
 def test_evict_indices_only(rkv):
     w = configs.TINY_FP32
     d = gen.prompt_layer(w)
