@@ -2,14 +2,14 @@
 // "Explanation of Calculating Approximate Attention Scores": select the pages with higher
 // scores; "Measurement of Exact-TopK": SnapKV's one-time top-k filter of the prompt).
 //
-// Rows of up to 8192 elements (page scores of a decode step): one 256-thread block per row holds
-// the row in registers and runs the block select of rkv_select.hpp. Longer rows (prompt token
-// scores) are spread over blocks of 4096 elements each, in six short launches: clear the
-// row histograms; three digit levels (bits 31..21, 20..10, 9..0 of the keys), each block
-// counting the digits of its keys that match the prefix found so far into the row's global
-// histogram (every block of the next launch re-derives that prefix from it); a per-block count
-// of the keys above and equal to the threshold; and the ordered write, where each block offsets
-// its block-level compaction by the counts of the blocks before it.
+// Rows of up to 8192 elements (page scores of a decode step): one block per row holds the row in
+// registers and runs the block select of rkv_select.hpp. Longer rows (prompt token scores) are
+// spread over blocks of 4096 elements each, in five short launches: clear the row histograms;
+// three digit levels (bits 31..21, 20..10, 9..0 of the keys), each block counting the digits of
+// its keys that match the prefix found so far into the row's global histogram (every block of
+// the next launch re-derives that prefix from it), the last level also leaving each block's own
+// counts under the prefix; and the ordered write, where each block fixes the threshold and
+// offsets its block-level compaction by the counts of the blocks before it.
 #include <algorithm>
 
 #include "rkv_common.hpp"
