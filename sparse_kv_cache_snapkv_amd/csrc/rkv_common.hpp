@@ -109,7 +109,7 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 
 // Non-temporal 16-byte store, for output written once and not read back by the same launch:
 // the channel-major page summaries (their 64-byte row segments run about 22% faster streamed
-// out) and the compacted K/V rows of the eviction (its gather about 6 us faster per 128K layer).
+// out) and the compacted K/V rows of the eviction.
 __device__ __forceinline__ void store16_stream(void* p, uint4 v) {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
   v4u w;
