@@ -484,6 +484,78 @@ __global__ __launch_bounds__(kThreads) void k_pool(const float* __restrict__ col
   pooled[(size_t)bh * n + j] = KIND == 0 ? acc / (float)kernel : acc;
 }
 
+// Box-average pooling fused with the first digit level of the multi-block kept-set top-k: a block
+// pools kPoolSpan consecutive positions of one row, thread t the kPoolPer positions from
+// kPoolPer * t by a sliding window (the first window summed in order, then one value in and one
+// out per step), and counts each output's top key bits into the row's first-level histogram
+// (already cleared), so the top-k skips that pass. The values differ from k_pool's direct box
+// sums only in rounding.
+constexpr int kPoolThreads = 1024;
+constexpr int kPoolPer = 4;
+constexpr int kPoolSpan = kPoolPer * kPoolThreads;
+
+__global__ __launch_bounds__(kPoolThreads) void k_pool_count(const float* __restrict__ colsum, int n,
+                                                         int parts, int kernel,
+                                                         float* __restrict__ pooled,
+                                                         uint32_t* __restrict__ hist0) {
+  __shared__ float tile[kPoolSpan + 128];
+  __shared__ uint32_t lh[kTopkLevel0Bins];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int h = kernel / 2;
+  const int j0 = blockIdx.x * kPoolSpan;
+  const float* src = colsum + (size_t)bh * n;
+  const size_t pstride = (size_t)gridDim.y * n;  // between the window-row parts' partial sums
+  for (int i = tid; i < kTopkLevel0Bins; i += kPoolThreads) lh[i] = 0u;
+  for (int i = tid; i < kPoolSpan + 2 * h; i += kPoolThreads) {
+    const int j = j0 - h + i;
+    const int jc = min(max(j, 0), n - 1);  // every address inside the row
+    float x = src[jc];
+    for (int p = 1; p < parts; ++p) x += src[p * pstride + jc];
+    tile[i] = (j >= 0 && j < n) ? x : 0.f;
+  }
+  __syncthreads();
+  const int jb = kPoolPer * tid;  // this thread's first position in the block
+  const float inv = 1.f / (float)kernel;
+  float sum = 0.f;
+  for (int u = 0; u < kernel; ++u) sum += tile[jb + u];
+  float v[kPoolPer];
+#pragma unroll
+  for (int m = 0; m < kPoolPer; ++m) {
+    v[m] = sum * inv;
+    sum += tile[jb + m + kernel] - tile[jb + m];
+  }
+  const int nv = min(kPoolPer, n - (j0 + jb));  // may be <= 0 past the row's end
+  float* out = pooled + (size_t)bh * n + j0 + jb;
+  if (nv == kPoolPer && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+#pragma unroll
+    for (int m = 0; m < kPoolPer; m += 4)
+      *reinterpret_cast<float4*>(out + m) = make_float4(v[m], v[m + 1], v[m + 2], v[m + 3]);
+  } else {
+    for (int m = 0; m < nv; ++m) out[m] = v[m];
+  }
+  // a thread's outputs are consecutive box averages, mostly in one top-bit bin: runs of equal
+  // bins are counted before one LDS addition each
+  if (nv > 0) {
+    uint32_t cur = order_key(v[0]) >> kTopkLevel0Shift, cnt = 1u;
+#pragma unroll
+    for (int m = 1; m < kPoolPer; ++m) {
+      if (m >= nv) break;
+      const uint32_t b = order_key(v[m]) >> kTopkLevel0Shift;
+      if (b != cur) {
+        atomicAdd(&lh[cur], cnt);
+        cur = b;
+        cnt = 0u;
+      }
+      ++cnt;
+    }
+    atomicAdd(&lh[cur], cnt);
+  }
+  __syncthreads();
+  uint32_t* hr = hist0 + (size_t)bh * kTopkHistRowWords;
+  for (int i = tid; i < kTopkLevel0Bins; i += kPoolThreads)
+    if (lh[i] != 0u) atomicAdd(&hr[i], lh[i]);
+}
+
 // Completes kept_idx (window positions, or the identity when nothing is evicted) and gathers
 // the compressed K/V rows, 16 bytes per lane.
 template <typename T, int D>
@@ -637,7 +709,12 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
   if (e != hipSuccess) return e;
   float* colsum = reinterpret_cast<float*>(w + lo.off_colsum);
   float* pooled = pooled_out != nullptr ? pooled_out : reinterpret_cast<float*>(w + lo.off_pooled);
-  if (pool_type == 0)
+  // average pooling ahead of the multi-block top-k also counts its first digit level
+  const bool counted = cleared && pool_type == 0;
+  if (counted)
+    hipLaunchKernelGGL(k_pool_count, dim3((n + kPoolSpan - 1) / kPoolSpan, BH), dim3(kPoolThreads),
+                       0, stream, colsum, n, lo.parts2, pool_kernel, pooled, hist);
+  else if (pool_type == 0)
     hipLaunchKernelGGL(k_pool<0>, dim3((n + kThreads - 1) / kThreads, BH), dim3(kThreads), 0,
                        stream, colsum, n, lo.parts2, pool_kernel, pooled);
   else
@@ -645,7 +722,7 @@ hipError_t launch_evict(const void* q_win, const void* k, const void* v, int B, 
                        stream, colsum, n, lo.parts2, pool_kernel, pooled);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   e = cleared ? launch_topk_cleared(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk,
-                                    stream)
+                                    counted, stream)
               : launch_topk(pooled, BH, n, keep - W, kept_idx, keep, w + lo.off_topk, stream);
   if (e != hipSuccess) return e;
   return gather_any(dtype, D, k, v, BH, L, W, keep, 0, kept_idx, k_out, v_out, stream);

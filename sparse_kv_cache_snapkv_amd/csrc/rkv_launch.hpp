@@ -37,13 +37,19 @@ size_t topk_ws_bytes(int rows, int n, int k);
 hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out, int out_stride,
                        void* ws, hipStream_t stream);
 // Rows that take the multi-block path keep their digit histograms in the first
-// topk_hist_words(rows) 32-bit words of the top-k workspace. A caller that has already cleared
-// them (in a launch of its own, as SnapKV++ eviction does) calls launch_topk_cleared, which skips
-// the clearing launch.
+// topk_hist_words(rows) 32-bit words of the top-k workspace, kTopkHistRowWords per row; a row's
+// first level counts the keys' top bits (order key >> kTopkLevel0Shift) in its first
+// kTopkLevel0Bins words. A caller that has already cleared them (in a launch of its own, as
+// SnapKV++ eviction does) calls launch_topk_cleared, which skips the clearing launch; one whose
+// producing kernel has also counted the first level (the eviction's pooling) passes
+// level0_counted, which skips that pass too.
+constexpr int kTopkHistRowWords = 3 * 2048;
+constexpr int kTopkLevel0Shift = 21;
+constexpr int kTopkLevel0Bins = 2048;
 bool topk_multiblock(int n, int k);
 size_t topk_hist_words(int rows);
 hipError_t launch_topk_cleared(const float* scores, int rows, int n, int k, int32_t* out,
-                               int out_stride, void* ws, hipStream_t stream);
+                               int out_stride, void* ws, bool level0_counted, hipStream_t stream);
 
 // Exact attention over the selected pages.
 size_t attend_ws_bytes(int B, int Hq, int Hkv, int D, int page_size, int n_pages, int dtype);

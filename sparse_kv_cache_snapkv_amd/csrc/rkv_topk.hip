@@ -57,6 +57,10 @@ __host__ __device__ constexpr int level_shift(int lev) { return lev == 0 ? 21 : 
 __host__ __device__ constexpr int level_bits(int lev) { return lev == 2 ? 10 : 11; }
 __host__ __device__ constexpr int level_bins(int lev) { return 1 << level_bits(lev); }
 
+static_assert(kLevels * kHistStride == kTopkHistRowWords && level_shift(0) == kTopkLevel0Shift &&
+                  level_bins(0) == kTopkLevel0Bins,
+              "the first digit level as declared to producers that count it");
+
 // Per block of the last digit level: the suffix sums S[d] (its keys under the row's prefix with
 // a last digit >= d, d < 1024) and, in word 1024, its keys above the prefix.
 constexpr int kLastBins = level_bins(kLevels - 1);
@@ -255,7 +259,8 @@ namespace {
 // The launches of the multi-block path; the clearing launch only where the histograms are not
 // already zero.
 hipError_t long_launches(const float* scores, int rows, int n, int k, int32_t* out,
-                         int out_stride, void* ws, bool cleared, hipStream_t stream) {
+                         int out_stride, void* ws, bool cleared, bool level0_counted,
+                         hipStream_t stream) {
   const LongLayout lo = long_layout(rows, n);
   char* w = static_cast<char*>(ws);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + lo.off_hist);
@@ -268,9 +273,11 @@ hipError_t long_launches(const float* scores, int rows, int n, int k, int32_t* o
                        dim3(256), 0, stream, hist, nhist);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_long_hist<0>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist,
-                     state);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!level0_counted) {
+    hipLaunchKernelGGL(k_long_hist<0>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist,
+                       state);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_long_hist<1>, lgrid, dim3(kBlockThreads), 0, stream, scores, n, k, hist,
                      state);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -285,8 +292,8 @@ hipError_t long_launches(const float* scores, int rows, int n, int k, int32_t* o
 }  // namespace
 
 hipError_t launch_topk_cleared(const float* scores, int rows, int n, int k, int32_t* out,
-                               int out_stride, void* ws, hipStream_t stream) {
-  return long_launches(scores, rows, n, k, out, out_stride, ws, true, stream);
+                               int out_stride, void* ws, bool level0_counted, hipStream_t stream) {
+  return long_launches(scores, rows, n, k, out, out_stride, ws, true, level0_counted, stream);
 }
 
 hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out, int out_stride,
@@ -308,7 +315,7 @@ hipError_t launch_topk(const float* scores, int rows, int n, int k, int32_t* out
                        dim3(kBlockThreads), 0, stream, out, n, out_stride);
     return hipGetLastError();
   }
-  return long_launches(scores, rows, n, k, out, out_stride, ws, false, stream);
+  return long_launches(scores, rows, n, k, out, out_stride, ws, false, false, stream);
 }
 
 }  // namespace rkv

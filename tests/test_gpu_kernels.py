@@ -299,6 +299,10 @@ def test_snapkvpp_evict_odd_key_groups_multiblock_topk(rkv):
     # the fp32 passes ahead of the same multi-block top-k
     wf = w.replace(name="odd-groups-fp32", dtype="fp32", B=2, L=9000, cfg_id=32)
     _evict_check(rkv, wf, gen.prompt_layer(wf))
+    # a prefix of 9001 scores: the pooling that counts the top-k's first digit level ends in a
+    # partial block, and the second row's scores start off a 16-byte boundary
+    wr = w.replace(name="odd-groups-ragged", B=2, L=9017, keep=1500, cfg_id=34)
+    _evict_check(rkv, wr, gen.prompt_layer(wr))
 
 
 # (G, W, D): window rows G*W from one 32-row tile to 16 tiles; 120 rows end in a partial tile,
