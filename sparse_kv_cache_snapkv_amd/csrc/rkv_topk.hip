@@ -90,22 +90,30 @@ __global__ void k_long_zero(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-// The digit of level `lev` holding the krem-th largest key of the keys counted in `hist` (the
-// row's histogram of that level, finished by an earlier launch), and how many counted keys lie in
-// higher digits. Every thread must call it; two barriers.
-__device__ __forceinline__ void find_digit(const uint32_t* __restrict__ hist, int nbins,
-                                           uint32_t krem, uint32_t& digit, uint32_t& above,
-                                           SelectShared<kBlockThreads>& sh) {
-  const int tid = threadIdx.x;
-  const int bpt = nbins / kBlockThreads;  // 8 or 4 digits per thread, descending
-  uint32_t c[8], local = 0;
+// This thread's bins of one level's histogram (a row's, finished by an earlier launch), 8 or 4
+// digits descending from nbins-1-bpt*tid; entries past the level's bins are 0.
+__device__ __forceinline__ void load_bins(const uint32_t* __restrict__ hist, int nbins,
+                                          uint32_t (&c)[8]) {
+  const int bpt = nbins / kBlockThreads;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int bin = nbins - 1 - (tid * bpt + j);  // negative only when j >= bpt
+    const int bin = nbins - 1 - ((int)threadIdx.x * bpt + j);  // negative only when j >= bpt
     const uint32_t x = hist[bin < 0 ? 0 : bin];
     c[j] = j < bpt ? x : 0u;
-    local += c[j];
   }
+}
+
+// The digit of a level (nbins digits, this thread's bins in c as load_bins leaves them) holding
+// the krem-th largest key of the keys it counts, and how many counted keys lie in higher digits.
+// Every thread must call it; two barriers.
+__device__ __forceinline__ void find_digit(const uint32_t (&c)[8], int nbins, uint32_t krem,
+                                           uint32_t& digit, uint32_t& above,
+                                           SelectShared<kBlockThreads>& sh) {
+  const int tid = threadIdx.x;
+  const int bpt = nbins / kBlockThreads;
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) local += c[j];
   uint32_t excl, unused, tot, unused2;
   block_scan2<kBlockThreads>(local, 0u, excl, unused, tot, unused2, sh, 0);
   if (excl < krem && krem <= excl + local) {
@@ -126,16 +134,24 @@ __device__ __forceinline__ void find_digit(const uint32_t* __restrict__ hist, in
 }
 
 // Re-derives the prefix (the key bits above level `upto`) and the rank still to place within it.
-__device__ __forceinline__ void long_prefix(const uint32_t* __restrict__ hist_row, int upto,
-                                            uint32_t k, uint32_t& prefix, uint32_t& krem,
+// The histograms of all the levels it walks are loaded together before the first digit is found.
+template <int UPTO>
+__device__ __forceinline__ void long_prefix(const uint32_t* __restrict__ hist_row, uint32_t k,
+                                            uint32_t& prefix, uint32_t& krem,
                                             SelectShared<kBlockThreads>& sh) {
   prefix = 0u;
   krem = k;
-  for (int lev = 0; lev < upto; ++lev) {
-    uint32_t d, above;
-    find_digit(hist_row + lev * kHistStride, level_bins(lev), krem, d, above, sh);
-    prefix |= d << level_shift(lev);
-    krem -= above;
+  if constexpr (UPTO > 0) {
+    uint32_t c[UPTO][8];
+#pragma unroll
+    for (int lev = 0; lev < UPTO; ++lev) load_bins(hist_row + lev * kHistStride, level_bins(lev), c[lev]);
+#pragma unroll
+    for (int lev = 0; lev < UPTO; ++lev) {
+      uint32_t d, above;
+      find_digit(c[lev], level_bins(lev), krem, d, above, sh);
+      prefix |= d << level_shift(lev);
+      krem -= above;
+    }
   }
 }
 
@@ -153,7 +169,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_long_hist(const float* __rest
   const int tid = threadIdx.x, row = blockIdx.y;
   uint32_t* hist_row = hist + (size_t)row * kLevels * kHistStride;
   uint32_t prefix, krem;
-  long_prefix(hist_row, LEVEL, (uint32_t)k, prefix, krem, sh);
+  long_prefix<LEVEL>(hist_row, (uint32_t)k, prefix, krem, sh);
   constexpr int shift = level_shift(LEVEL), nbins = level_bins(LEVEL);
   constexpr int top = shift + level_bits(LEVEL);  // the digit's highest bit + 1
   for (int i = tid; i < nbins; i += kBlockThreads) lh[i] = 0u;
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_long_write(const float* __res
   __shared__ SelectShared<kBlockThreads> sh;
   const int tid = threadIdx.x, row = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
   uint32_t T, need;
-  long_prefix(hist + (size_t)row * kLevels * kHistStride, kLevels, (uint32_t)k, T, need, sh);
+  long_prefix<kLevels>(hist + (size_t)row * kLevels * kHistStride, (uint32_t)k, T, need, sh);
   const uint32_t d = T & (uint32_t)(kLastBins - 1);  // T's last digit
   uint32_t bgt = 0, beq = 0;
   for (int b = tid; b < blk; b += kBlockThreads) {
