@@ -1,5 +1,6 @@
-"""Host emulation of the address arithmetic of the fused decode step (k_decode_step) and of the
-page-summary kernel (k_page_minmax), at the shapes the benchmark runs: the 128K 8B-shaped layer
+"""Host emulation of the address arithmetic of the fused decode step (k_decode_step), of the
+page-summary kernel (k_page_minmax) and of the eviction's pooling (k_pool_count), at the shapes the
+benchmark runs: the 128K 8B-shaped layer
 over the compressed cache and over the multi-turn view of the full 131072-token cache (row map,
 cache pitch L), the batch-16 layer (128 heads) and the 80-layer 70B-shaped stack (640 heads).
 
@@ -259,6 +260,37 @@ def test_page_minmax_indices_stay_in_their_buffers(shape):
                     < BH * kv_rows * D).all()
         np_ = min(pages_per_block, P - p0)
         assert (BH - 1) * D * s_pitch + p0 + (D - 1) * s_pitch + np_ - 1 < BH * D * s_pitch
+
+
+@pytest.mark.parametrize("kernel", [1, 3, 15, 31, 63, 127])
+@pytest.mark.parametrize("n", [8193, 9001, 131040, 262080])
+def test_pool_count_indices_stay_in_their_buffers(kernel, n):
+    # k_pool_count (rkv_evict.hip): blocks of SPAN positions, THREADS_P threads of PER consecutive
+    # outputs; the LDS tile holds SPAN + 128 floats, staged from position j0 - h for SPAN + 2h
+    # entries. The sliding window reads tile[jb + m + kernel] after output m; only the reads that
+    # feed an output must be staged, the last one only has to stay inside the tile.
+    THREADS_P, PER = 1024, 4
+    SPAN = THREADS_P * PER
+    TILE = SPAN + 128
+    h = kernel // 2
+    staged = SPAN + 2 * h
+    assert staged <= TILE
+    jb = PER * np.arange(THREADS_P)
+    first = jb[:, None] + np.arange(kernel)[None, :]  # the first window
+    assert first.max() < staged
+    for m in range(PER):
+        out_in, out_out = jb + m + kernel, jb + m  # the slide after output m
+        assert out_in.max() < TILE and out_out.max() < staged
+        if m < PER - 1:  # feeds output m + 1
+            assert out_in.max() < staged
+    # global reads: positions j0 - h + i clamped into [0, n); writes: positions below n only
+    nblk = -(-n // SPAN)
+    for bx in (0, nblk - 1):
+        j0 = bx * SPAN
+        j = j0 - h + np.arange(staged)
+        assert (np.clip(j, 0, n - 1) < n).all()
+        nv = np.minimum(PER, n - (j0 + jb))
+        assert ((j0 + jb + np.maximum(nv, 0) - 1)[nv > 0] < n).all()
 
 
 def test_library_plans_of_the_benchmarked_workloads():
