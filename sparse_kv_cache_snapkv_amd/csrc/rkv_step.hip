@@ -119,6 +119,8 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   a.kv_pitch = kv_pitch;
   a.rows = rows;
   a.s_pitch = Pcap;
+  // blocks y * BH + x of head x share an XCD exactly when BH is a multiple of the XCD count
+  a.xcd_local = BH % step::kXcds == 0 ? 1 : 0;
   a.scale2 = scale * kLog2e;
   const char* steal_env = getenv("RKV_STEAL_US");
   const long long steal_us = steal_env != nullptr ? atol(steal_env) : kStealMicroseconds;

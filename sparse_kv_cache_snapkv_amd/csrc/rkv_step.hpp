@@ -14,12 +14,19 @@
 // the owner's, so work done twice is harmless. So a call finishes however its blocks are
 // scheduled, also while other kernels hold CUs, and it needs no counter on its critical path.
 //
-// Exchange. Scores and partials cross blocks as 64-bit words {value bits, epoch} written and read
-// with device-coherent relaxed atomics; a reader re-reads a word until its tag is the current
-// epoch, so no fence or flag orders anything. Each block reads the head's stored epoch at its
-// start and then counts itself as started; the block that finds it was the last to start (at its
-// end, so the count's round trip delays nobody) stores the new epoch and clears the count: by
-// then every block of the head has read the old epoch, and no block of the call reads it again.
+// Exchange. Scores and partials cross blocks as 64-bit words {value bits, epoch}, read with
+// device-coherent relaxed atomic loads, which pass the CU's own cache; a reader re-reads a word
+// until its tag is the current epoch, so no fence or flag orders anything. Where every block of a
+// head runs on one XCD (a.xcd_local), the words are written with workgroup-scope stores: the CU's
+// cache writes through into the XCD's L2, which those loads read, so no word travels past that L2.
+// The memory model does not promise another block that visibility; the cache arrangement gives it,
+// and a word that never showed up would only cost the steal deadline (below), not a wrong value: a
+// block's re-reads of words its own threads wrote are within the stores' scope. Elsewhere the words
+// are written device-coherently.
+// Each block reads the head's stored epoch at its start and then counts itself as started; the
+// block that finds it was the last to start (at its end, so the count's round trip delays nobody)
+// stores the new epoch and clears the count: by then every block of the head has read the old
+// epoch, and no block of the call reads it again.
 //
 // One-block heads (nb = 1: heads of at most 128 pages, or more heads than fit two blocks each)
 // score into LDS and exchange nothing. Over kTargetBlocks heads the step does not use this kernel
@@ -49,6 +56,7 @@ constexpr int kMaxScorers = 64;
 // (one for 128 pages, with no exchange at all), as each share costs a full exchange round trip.
 constexpr int kMinScorePages = 128;
 constexpr int kTargetBlocks = 256;   // CUs of an MI355X: the grid of a waiting plan fits them
+constexpr int kXcds = 8;             // XCDs of an MI355X, dealt blocks round-robin by linear id
 constexpr int kSyncHeader = 16;      // words before the per-head words; word 0 is the status
 constexpr int kHeadWords = 4;        // per head: epoch, started count, two spare
 
@@ -72,6 +80,7 @@ struct Args {
   int kv_pitch;          // token slots per head of k_c, v_c (>= Lc; the full length L with rows)
   const int32_t* rows;   // optional [BH, Lc]: slot t of head bh is row rows[bh*Lc + t] of k_c, v_c
   int s_pitch;           // pages per channel row of the summaries (>= P)
+  int xcd_local;         // every block of a head runs on one XCD (exchange words stay in its L2)
   float scale2;          // softmax scale * log2(e)
   long long steal_ticks; // wait before a block does missing work itself (steady-counter
                          // ticks); negative: it does all of it itself (a test mode)
@@ -95,8 +104,19 @@ template <typename V>
 __device__ __forceinline__ void st_coherent(V* p, V v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned add_coherent(unsigned* p, unsigned v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// An exchange word, written as described at the top of this file.
+template <typename V>
+__device__ __forceinline__ void st_exchange(V* p, V v, bool xcd_local) {
+  if (xcd_local)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    st_coherent(p, v);
+}
+// *p + 1, returning the old value. An increment rather than an add: the compiler turns a
+// wave-uniform atomic add into a wave-wide one whose result it waits for at once, which would put
+// the atomic's round trip in front of the block's next barrier.
+__device__ __forceinline__ unsigned inc_coherent(unsigned* p) {
+  return __builtin_amdgcn_atomic_inc32(p, 0xffffffffu, __ATOMIC_RELAXED, "agent");
 }
 __device__ __forceinline__ void set_status(unsigned* status, unsigned flag) {
   __hip_atomic_fetch_or(status, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -158,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
   __shared__ StridedShared<kThreads, E> ssel;
   __shared__ unsigned s_miss_lo, s_miss_hi;
   AttendShared<D, G, kWaves>& sh = u.att;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x;
   // grid (BH, nb): consecutive blocks belong to different heads, so the round-robin placement of
   // blocks on the XCDs keeps every block of a head on one XCD when BH is a multiple of 8
   const int bh = blockIdx.x, y = blockIdx.y, b = bh / a.Hkv, h = bh % a.Hkv;
@@ -193,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
     const int pb_lo = j * a.ppb1, pb_hi = min(a.P, pb_lo + a.ppb1);
     auto sink = [&](int p, float v) {
       if (multi)
-        st_coherent(xs + p, tagged(__float_as_uint(v), epoch));
+        st_exchange(xs + p, tagged(__float_as_uint(v), epoch), a.xcd_local != 0);
       else
         u.scores[p] = v;
       if (pso != nullptr) pso[p] = v;
@@ -212,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
   auto count_started = [&]() {
     if (multi && tid == 0) {
       asm volatile("" ::"v"(epoch_prev));
-      started = add_coherent(hw + 1, 1u);
+      started = inc_coherent(hw + 1);
     }
   };
 
@@ -332,10 +352,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
         const int g = idx / D, c = idx % D;
         float M, lsum, o;
         wave_merge<D, G, kWaves>(sh, g, c, M, lsum, o);
-        st_coherent(mine + idx, tagged(__float_as_uint(o), epoch));
+        st_exchange(mine + idx, tagged(__float_as_uint(o), epoch), a.xcd_local != 0);
         if (c == 0) {
-          st_coherent(mine + G * D + g, tagged(__float_as_uint(M), epoch));
-          st_coherent(mine + G * D + G + g, tagged(__float_as_uint(lsum), epoch));
+          st_exchange(mine + G * D + g, tagged(__float_as_uint(M), epoch), a.xcd_local != 0);
+          st_exchange(mine + G * D + G + g, tagged(__float_as_uint(lsum), epoch), a.xcd_local != 0);
         }
       }
     };
