@@ -121,6 +121,13 @@ hipError_t launch_decode_step(const void* q, const void* kmin_t, const void* kma
   a.s_pitch = Pcap;
   // blocks y * BH + x of head x share an XCD exactly when BH is a multiple of the XCD count
   a.xcd_local = BH % step::kXcds == 0 ? 1 : 0;
+  // Blocks that only score touch their share's best pages ahead of the attention where the budget
+  // is small (its first loads are then on the critical path) and the lines land in the L2 that
+  // the attenders read.
+  a.pf = pl.nb > 1 && a.xcd_local && n_pages < P && n_pages * page_size <= step::kPrefetchTokens &&
+                 pl.ppb1 <= step::kPrefetchShare
+             ? std::min(step::kPrefetchPages, 2 * ((n_pages + pl.ns - 1) / pl.ns))
+             : 0;
   a.scale2 = scale * kLog2e;
   const char* steal_env = getenv("RKV_STEAL_US");
   const long long steal_us = steal_env != nullptr ? atol(steal_env) : kStealMicroseconds;

@@ -57,6 +57,11 @@ constexpr int kMaxScorers = 64;
 constexpr int kMinScorePages = 128;
 constexpr int kTargetBlocks = 256;   // CUs of an MI355X: the grid of a waiting plan fits them
 constexpr int kXcds = 8;             // XCDs of an MI355X, dealt blocks round-robin by linear id
+// Touching ahead (Args::pf): budgets up to kPrefetchTokens tokens, shares up to kPrefetchShare
+// pages (the share is ranked in LDS, one page per thread against all), at most kPrefetchPages.
+constexpr int kPrefetchTokens = 512;
+constexpr int kPrefetchShare = 256;
+constexpr int kPrefetchPages = 8;
 constexpr int kSyncHeader = 16;      // words before the per-head words; word 0 is the status
 constexpr int kHeadWords = 4;        // per head: epoch, started count, two spare
 
@@ -81,6 +86,8 @@ struct Args {
   const int32_t* rows;   // optional [BH, Lc]: slot t of head bh is row rows[bh*Lc + t] of k_c, v_c
   int s_pitch;           // pages per channel row of the summaries (>= P)
   int xcd_local;         // every block of a head runs on one XCD (exchange words stay in its L2)
+  int pf;                // pages of its own share whose K/V rows a block that only scores touches
+                         // after scoring (0: none)
   float scale2;          // softmax scale * log2(e)
   long long steal_ticks; // wait before a block does missing work itself (steady-counter
                          // ticks); negative: it does all of it itself (a test mode)
@@ -208,14 +215,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
   float* pso = a.page_scores != nullptr ? a.page_scores + (size_t)bh * a.P : nullptr;
   uint64_t* xs = a.xscores + (size_t)bh * a.P;
 
-  // Scores share j: published as tagged words (or into LDS for a one-block head).
+  // Scores share j: published as tagged words, and kept in LDS (for a one-block head, its
+  // selection's input; otherwise the touch ahead's, ahead of any other use of that LDS).
+  const bool keep_share = multi && y >= a.na && y < a.ns && a.pf > 0 && a.ppb1 <= kPrefetchShare;
   auto score_share = [&](int j) {
     const int pb_lo = j * a.ppb1, pb_hi = min(a.P, pb_lo + a.ppb1);
     auto sink = [&](int p, float v) {
-      if (multi)
+      if (multi) {
         st_exchange(xs + p, tagged(__float_as_uint(v), epoch), a.xcd_local != 0);
-      else
+        u.scores[p - pb_lo] = v;  // read back only by a block that touches ahead
+      } else {
         u.scores[p] = v;
+      }
       if (pso != nullptr) pso[p] = v;
     };
     if (a.vec)
@@ -241,6 +252,53 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(Args a) {
     if (a.chan_idx != nullptr && y == 0)
       for (int j = tid; j < a.r; j += kThreads) a.chan_idx[(size_t)bh * a.r + j] = ch.chan[j];
     score_share(y);
+    if (keep_share) {
+      // Touch ahead: the K/V rows of this share's pf best pages are loaded and dropped, so that
+      // the attenders (on the same XCD) find them in its L2. The attention at small budgets waits
+      // on its first loads; this block would otherwise idle until the step ends. A page's rank
+      // counts the share's higher scores (and equal ones at lower index), so ranks are distinct.
+      const int pb_lo = y * a.ppb1, nsh = min(a.P, pb_lo + a.ppb1) - pb_lo;
+      const int m = min(nsh, a.pf);
+      int* best = reinterpret_cast<int*>(mg.o);  // unused by a block that does not attend
+      const int nsh4 = (nsh + 3) & ~3;  // read four at a time; the padding never outranks
+      if (tid < nsh4 - nsh) u.scores[nsh + tid] = -INFINITY;
+      lds_barrier();
+      for (int t = tid; t < nsh; t += kThreads) {
+        const float v = u.scores[t];
+        int rank = 0;
+#pragma unroll 2
+        for (int i = 0; i < nsh4; i += 4) {
+          const float4 w = *reinterpret_cast<const float4*>(&u.scores[i]);
+          rank += (w.x > v || (w.x == v && i < t)) ? 1 : 0;
+          rank += (w.y > v || (w.y == v && i + 1 < t)) ? 1 : 0;
+          rank += (w.z > v || (w.z == v && i + 2 < t)) ? 1 : 0;
+          rank += (w.w > v || (w.w == v && i + 3 < t)) ? 1 : 0;
+        }
+        if (rank < m) best[rank] = pb_lo + t;
+      }
+      lds_barrier();
+      const T* kc_bh = static_cast<const T*>(a.k_c) + (size_t)bh * a.kv_pitch * D;
+      const T* vc_bh = static_cast<const T*>(a.v_c) + (size_t)bh * a.kv_pitch * D;
+      const int32_t* rows_bh = a.rows != nullptr ? a.rows + (size_t)bh * a.Lc : nullptr;
+      constexpr int kChunks = (int)(D * sizeof(T) / 16);  // 16-byte pieces of a row
+      const int wave = tid / kWave, lane = tid % kWave;
+      uint32_t sink = 0u;
+#pragma unroll 1
+      for (int e = wave; e < m; e += kWaves) {
+        const int p = best[e];
+        if (p < pb_lo || p >= pb_lo + nsh) continue;  // a NaN score can leave a rank unfilled
+#pragma unroll 1
+        for (int i = lane; i < a.ps * kChunks; i += kWave) {
+          const int t = p * a.ps + i / kChunks;
+          if (t >= a.Lc) continue;
+          const int row = rows_bh != nullptr ? min(max(rows_bh[t], 0), a.kv_pitch - 1) : t;
+          const uint4 kx = load16(kc_bh + (size_t)row * D + (i % kChunks) * (16 / sizeof(T)));
+          const uint4 vx = load16(vc_bh + (size_t)row * D + (i % kChunks) * (16 / sizeof(T)));
+          sink ^= kx.x ^ kx.y ^ kx.z ^ kx.w ^ vx.x ^ vx.y ^ vx.z ^ vx.w;
+        }
+      }
+      asm volatile("" ::"v"(sink));  // the loads stay: their values are consumed
+    }
   }
 
   if (y < a.na) {

@@ -22,6 +22,15 @@ SOLO_TOKENS, TOKENS_PER_BLOCK = 256, 64
 SYNC_HEADER, HEAD_WORDS = 16, 4
 MAX_PAGES_PER_WINDOW = 1024
 MIN_SCORE_PAGES = 128
+XCDS = 8
+PREFETCH_TOKENS, PREFETCH_SHARE, PREFETCH_PAGES = 512, 256, 8
+
+
+def prefetch_pages(BH, P, ps, n_pages, pl):
+    # pages of its share that a block which only scores touches ahead (rkv_step.hip)
+    ok = (pl["nb"] > 1 and BH % XCDS == 0 and n_pages < P and n_pages * ps <= PREFETCH_TOKENS
+          and pl["ppb1"] <= PREFETCH_SHARE)
+    return min(PREFETCH_PAGES, 2 * -(-n_pages // pl["ns"])) if ok else 0
 
 
 def plan(BH, P, ps, n_pages, ncu, vmax):
@@ -185,6 +194,21 @@ def test_fused_step_indices_stay_in_their_buffers(shape, ncu):
                     if nb > 1:
                         assert bh * P + pb_hi - 1 < BH * Pcap  # tagged scores
                         assert (bh * P + pb_hi - 1) * 8 + lo["off_xscores"] < lo["off_xpart"]
+                pf = prefetch_pages(BH, P, ps, n_pages, pl)
+                if pf > 0 and na <= y < ns:
+                    # touch ahead: the share's scores in LDS (E * THREADS floats, padded to a
+                    # multiple of four), the ranks'
+                    # page list in the merge area (G * D + MAX_ATT words), then the 16-byte
+                    # pieces of the K/V rows of pages p in [pb_lo, pb_lo + nsh), slots t < Lc
+                    nsh = min(P, y * ppb1 + ppb1) - y * ppb1
+                    assert nsh <= PREFETCH_SHARE and nsh + 3 <= E * THREADS  # with its -inf padding
+                    assert min(nsh, pf) <= G * D + MAX_ATT
+                    chunks = D // V
+                    i = np.arange(ps * chunks)
+                    t = ((y * ppb1 + nsh - 1) * ps + i // chunks)
+                    t = t[t < Lc] if (t < Lc).any() else np.array([0])
+                    row = np.full_like(t, kv_rows - 1) if rows_mapped else t
+                    assert ((bh * kv_rows + row) * D + (i[: len(row)] % chunks) * V + V - 1).max() < BH * kv_rows * D
                 if y >= na:
                     continue
                 # attender: every score word; a stale one marks share (page / ppb1) < ns
